@@ -1,0 +1,318 @@
+"""Oracle for causal kernelized linear attention (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never links, loads
+or calls it, and it shares no code with the HIP path: the seeded input
+generators live in a module of their own and hold none of the method's
+arithmetic.
+
+Source of truth is the page "Linear attention：把历史写进状态"
+(hs-black.github.io/posts/linear-attention).  Contents:
+
+* :func:`recurrence` -- the oracle proper, the plain FP64 token-by-token
+  recurrence (sections "每来一个 token，更新两个累加器", "查询时，分子和分母一起读",
+  "ε 是数值保护", "加一个门" and "最小递推里，每一行都有张量意义"), written in
+  plain C (``linattn_oracle.c``) and called through ctypes.
+* :func:`quadratic_masked` -- the quadratic masked form A = (Q~K~^T) * M,
+  Y = AV / rowsum(A) of section "先确认我们在重排哪一种 attention", with the gate
+  entering as the products of later gates (exercise 2's coefficients
+  [a2*a3, a3, 1]).  Brute force; an independent formula used to pin the
+  recurrence.
+* :func:`chunkwise` -- the chunk equations of section "一个 chunk 的输出由两部分
+  组成", with the gated extension the page asks for ("门控版本要加入门乘积")
+  written as explicit gate products.
+* :func:`scan_prefix` -- the affine composition (a2, B2) o (a1, B1) =
+  (a2 a1, a2 B1 + B2) of section "门控递推为什么能做并行 scan", combined in
+  tree order.
+
+Every function here is pinned by the CPU tests against the page's worked
+examples, closed forms and brute force (see ``tests/test_oracle_pins.py``).
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "linattn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblinattn_oracle.so")
+
+PHI_ELU1 = 0
+PHI_IDENTITY = 1
+_PHI_MODES = {"elu1": PHI_ELU1, "identity": PHI_IDENTITY}
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def build_oracle(force: bool = True) -> str:
+    """Compile ``linattn_oracle.c`` into ``liblinattn_oracle.so`` with gcc.
+
+    No fast-math and no floating-point contraction: the C arithmetic is the
+    arithmetic written in the source.
+    """
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            build_oracle(force=False)
+            lib = ctypes.CDLL(_LIB_PATH)
+            dp = ctypes.POINTER(ctypes.c_double)
+            lib.oracle_recurrence.restype = ctypes.c_int
+            lib.oracle_recurrence.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                              dp, dp, dp, dp, ctypes.c_double, ctypes.c_int32,
+                                              dp, dp, dp, dp]
+            lib.oracle_phi.restype = ctypes.c_double
+            lib.oracle_phi.argtypes = [ctypes.c_double]
+            _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def phi(x) -> np.ndarray:
+    """ELU(x)+1 with ELU's scale 1: x+1 for x > 0, exp(x) otherwise."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def phi_scalar_c(x: float) -> float:
+    """The C oracle's own feature map, for pinning it to the closed form."""
+    return _load().oracle_phi(float(x))
+
+
+def _features(x: np.ndarray, phi_mode: str) -> np.ndarray:
+    if phi_mode == "identity":
+        return np.asarray(x, dtype=np.float64)
+    if phi_mode == "elu1":
+        return phi(x)
+    raise ValueError("phi_mode must be 'elu1' or 'identity'")
+
+
+def recurrence(q, k, v, alpha=None, eps: float = 1e-6, S0=None, z0=None,
+               phi_mode: str = "elu1"):
+    """The oracle: FP64 token-by-token recurrence for one sequence.
+
+    q, k: [T, r]; v: [T, dv]; alpha: [T] or None (ungated); S0: [r, dv] and
+    z0: [r] (default zero).  Returns ``(Y [T, dv], S [r, dv], z [r], den [T])``
+    where ``den`` is phi(q_t)^T z_t before eps is added.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 2 or k.shape != q.shape or v.ndim != 2 or v.shape[0] != q.shape[0] or q.shape[0] == 0:
+        raise ValueError("q, k must be [T, r] of equal shape and v [T, dv] with the same T >= 1")
+    T, r = q.shape
+    dv = v.shape[1]
+    if r == 0 or dv == 0:
+        raise ValueError("feature and value widths must be >= 1")
+    a = None if alpha is None else _f64(alpha).reshape(T)
+    S = np.zeros((r, dv)) if S0 is None else _f64(S0).reshape(r, dv).copy()
+    z = np.zeros(r) if z0 is None else _f64(z0).reshape(r).copy()
+    y = np.empty((T, dv))
+    den = np.empty(T)
+    if phi_mode not in _PHI_MODES:
+        raise ValueError("phi_mode must be 'elu1' or 'identity'")
+    rc = _load().oracle_recurrence(T, r, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(a), float(eps),
+                                   _PHI_MODES[phi_mode], _ptr(S), _ptr(z), _ptr(y), _ptr(den))
+    if rc != 0:
+        raise RuntimeError("oracle_recurrence rejected its arguments")
+    return y, S, z, den
+
+
+def recurrence_heads(Q, K, V, alpha=None, eps: float = 1e-6, S0=None, z0=None,
+                     phi_mode: str = "elu1", threads: int = 1):
+    """:func:`recurrence` over independent heads.
+
+    Q, K: [..., T, r]; V: [..., T, dv]; alpha: [..., T] or None; S0: [..., r, dv];
+    z0: [..., r].  Heads are independent, so ``threads`` > 1 runs them on a
+    thread pool (ctypes releases the GIL during the C call).
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    lead = Q.shape[:-2]
+    T, r = Q.shape[-2:]
+    dv = V.shape[-1]
+    n = int(np.prod(lead)) if lead else 1
+    Qf, Kf, Vf = Q.reshape(n, T, r), K.reshape(n, T, r), V.reshape(n, T, dv)
+    Af = None if alpha is None else _f64(alpha).reshape(n, T)
+    Sf = None if S0 is None else _f64(S0).reshape(n, r, dv)
+    zf = None if z0 is None else _f64(z0).reshape(n, r)
+    Y = np.empty((n, T, dv))
+    S = np.empty((n, r, dv))
+    z = np.empty((n, r))
+    den = np.empty((n, T))
+
+    def one(h):
+        Y[h], S[h], z[h], den[h] = recurrence(
+            Qf[h], Kf[h], Vf[h], None if Af is None else Af[h], eps,
+            None if Sf is None else Sf[h], None if zf is None else zf[h], phi_mode)
+
+    if threads <= 1 or n == 1:
+        for h in range(n):
+            one(h)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(n)))
+    return (Y.reshape(*lead, T, dv), S.reshape(*lead, r, dv), z.reshape(*lead, r),
+            den.reshape(*lead, T))
+
+
+def gate_products(alpha, T: int) -> np.ndarray:
+    """D[t, i] = alpha[i+1] * ... * alpha[t] for i <= t (empty product 1), 0 above.
+
+    The weight the gate leaves on token i's write when token t reads (the
+    coefficients [a2*a3, a3, 1] of exercise 2).  Built by explicit products.
+    """
+    D = np.zeros((T, T))
+    for i in range(T):
+        D[i, i] = 1.0
+        for t in range(i + 1, T):
+            D[t, i] = D[t - 1, i] * (1.0 if alpha is None else float(alpha[t]))
+    return D
+
+
+def decay_from_start(alpha, T: int) -> np.ndarray:
+    """c[t] = alpha[0] * ... * alpha[t]: the weight left on the incoming state at token t."""
+    c = np.empty(T)
+    acc = 1.0
+    for t in range(T):
+        acc = acc * (1.0 if alpha is None else float(alpha[t]))
+        c[t] = acc
+    return c
+
+
+def quadratic_masked(q, k, v, alpha=None, eps: float = 1e-6, S0=None, z0=None,
+                     phi_mode: str = "elu1"):
+    """Brute-force quadratic form: A = (Q~ K~^T) * M (times gate products),
+    Y = (c * Q~ S0 + A V) / (c * Q~ z0 + rowsum(A) + eps).
+
+    With S0 = z0 = 0 and no gate this is exactly Y = AV / (rowsum(A) + eps).
+    Returns ``(Y, den)``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T = q.shape[0]
+    qf, kf = _features(q, phi_mode), _features(k, phi_mode)
+    A = (qf @ kf.T) * gate_products(alpha, T)
+    num = A @ v
+    den = A.sum(axis=1)
+    if S0 is not None or z0 is not None:
+        c = decay_from_start(alpha, T)
+        if S0 is not None:
+            num = num + c[:, None] * (qf @ _f64(S0))
+        if z0 is not None:
+            den = den + c * (qf @ _f64(z0))
+    return num / (den + eps)[:, None], den
+
+
+def chunkwise(q, k, v, alpha=None, eps: float = 1e-6, chunk: int = 64, S0=None, z0=None,
+              phi_mode: str = "elu1"):
+    """FP64 chunkwise form.  Per chunk c with incoming S_prev, z_prev:
+
+    num    = g * (Q~c S_prev) + [(Q~c K~c^T) * D] Vc
+    den    = g * (Q~c z_prev) + rowsum[(Q~c K~c^T) * D]
+    S_next = g_last * S_prev + K~c^T (w * Vc)
+    z_next = g_last * z_prev + sum_i w_i K~c[i]
+
+    where D holds the in-chunk gate products (the causal mask M when ungated),
+    g[j] the product of the chunk's gates up to token j, and w[i] = D[last, i].
+    Returns ``(Y, S, z, den)``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, r = q.shape
+    dv = v.shape[1]
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    qf, kf = _features(q, phi_mode), _features(k, phi_mode)
+    S = np.zeros((r, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros(r) if z0 is None else _f64(z0).copy()
+    Y = np.empty((T, dv))
+    den_all = np.empty(T)
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        n = t1 - t0
+        a = None if alpha is None else np.asarray(alpha, dtype=np.float64)[t0:t1]
+        D = gate_products(a, n)
+        g = decay_from_start(a, n)
+        Qc, Kc, Vc = qf[t0:t1], kf[t0:t1], v[t0:t1]
+        A = (Qc @ Kc.T) * D
+        num = g[:, None] * (Qc @ S) + A @ Vc
+        den = g * (Qc @ z) + A.sum(axis=1)
+        Y[t0:t1] = num / (den + eps)[:, None]
+        den_all[t0:t1] = den
+        w = D[n - 1]
+        S = g[n - 1] * S + Kc.T @ (w[:, None] * Vc)
+        z = g[n - 1] * z + (w[:, None] * Kc).sum(axis=0)
+    return Y, S, z, den_all
+
+
+def compose(later, earlier):
+    """(a2, B2, b2) o (a1, B1, b1) = (a2 a1, a2 B1 + B2, a2 b1 + b2).
+
+    Applying ``earlier`` then ``later`` to a state; b is the normaliser part
+    (B with k~ in place of k~ v^T).
+    """
+    a2, B2, b2 = later
+    a1, B1, b1 = earlier
+    return (a2 * a1, a2 * B1 + B2, a2 * b1 + b2)
+
+
+def scan_prefix(q, k, v, alpha=None, eps: float = 1e-6, S0=None, z0=None,
+                phi_mode: str = "elu1", order: str = "correct"):
+    """Inclusive prefix of the per-token affine maps by recursive doubling
+    (a tree order of composition, not the sequential one), then the read-out.
+
+    ``order='swapped'`` composes earlier o later instead; it exists only so
+    the tests can show that the order of composition matters.
+    Returns ``(Y, S, z, den)``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, r = q.shape
+    dv = v.shape[1]
+    qf, kf = _features(q, phi_mode), _features(k, phi_mode)
+    cur = []
+    for t in range(T):
+        a_t = 1.0 if alpha is None else float(alpha[t])
+        cur.append((a_t, np.outer(kf[t], v[t]), kf[t].copy()))
+    off = 1
+    while off < T:
+        nxt = list(cur)
+        for t in range(off, T):
+            if order == "correct":
+                nxt[t] = compose(cur[t], cur[t - off])
+            else:
+                nxt[t] = compose(cur[t - off], cur[t])
+        cur = nxt
+        off *= 2
+    S_in = np.zeros((r, dv)) if S0 is None else _f64(S0)
+    z_in = np.zeros(r) if z0 is None else _f64(z0)
+    Y = np.empty((T, dv))
+    den = np.empty(T)
+    for t in range(T):
+        a_t, B_t, b_t = cur[t]
+        S_t = a_t * S_in + B_t
+        z_t = a_t * z_in + b_t
+        den[t] = qf[t] @ z_t
+        Y[t] = (qf[t] @ S_t) / (den[t] + eps)
+    a_T, B_T, b_T = cur[T - 1]
+    return Y, a_T * S_in + B_T, a_T * z_in + b_T, den

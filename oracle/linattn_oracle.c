@@ -1,0 +1,104 @@
+/*
+ * Oracle for causal kernelized linear attention: plain FP64, one token at a time.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * do.  It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes follows the page "Linear attention：把历史写进状态"
+ * (hs-black.github.io/posts/linear-attention):
+ *   - feature map phi = ELU(x)+1 (section "关键改写：让求和先发生"), with ELU's
+ *     scale 1, i.e. phi(x) = x+1 for x > 0 and exp(x) for x <= 0;
+ *   - the two accumulators S (r x dv, feature-major) and z (r), starting from
+ *     whatever state the caller passes (zero for a fresh sequence, section
+ *     "每来一个 token，更新两个累加器"), updated first and read second so that
+ *     y_t includes token t (same section);
+ *   - the scalar forget gate of section "加一个门": the old S and z are both
+ *     multiplied by alpha_t before token t is written (alpha == NULL means
+ *     alpha_t = 1, the plain accumulating form of section "公式里的每个维度");
+ *   - the read-out y_t = (phi(q_t)^T S_t) / (phi(q_t)^T z_t + eps), with eps added
+ *     to the denominator (section "ε 是数值保护"), never max(den, eps).
+ * The same page's minimal FP64 loop (section "最小递推里，每一行都有张量意义")
+ * is exactly this recurrence with alpha = 1.
+ *
+ * Sums run left to right over the feature index.  Build without fast-math and
+ * without floating-point contraction so that the arithmetic is what is written.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define ORACLE_PHI_ELU1 0     /* phi(x) = ELU(x) + 1 */
+#define ORACLE_PHI_IDENTITY 1 /* the inputs already are features (worked examples) */
+
+double oracle_phi(double x)
+{
+    return x > 0.0 ? x + 1.0 : exp(x);
+}
+
+static double apply_feature_map(double x, int32_t phi_mode)
+{
+    return phi_mode == ORACLE_PHI_IDENTITY ? x : oracle_phi(x);
+}
+
+/*
+ * One sequence (one head).  Row-major arrays:
+ *   q, k  [T, r]      raw queries/keys (phi is applied here)
+ *   v     [T, dv]
+ *   alpha [T] or NULL
+ *   S     [r, dv]     in: state before token 0, out: state after token T-1
+ *   z     [r]         in/out like S
+ *   y     [T, dv]     out
+ *   den   [T] or NULL out: phi(q_t)^T z_t without eps (for denominator monitoring)
+ * Returns 0, or -1 on a bad argument or allocation failure (then nothing is written).
+ */
+int oracle_recurrence(int64_t T, int32_t r, int32_t dv,
+                      const double *q, const double *k, const double *v,
+                      const double *alpha, double eps, int32_t phi_mode,
+                      double *S, double *z, double *y, double *den)
+{
+    if (T < 1 || r < 1 || dv < 1 || !q || !k || !v || !S || !z || !y)
+        return -1;
+    if (phi_mode != ORACLE_PHI_ELU1 && phi_mode != ORACLE_PHI_IDENTITY)
+        return -1;
+
+    double *qf = (double *)malloc(sizeof(double) * (size_t)r);
+    double *kf = (double *)malloc(sizeof(double) * (size_t)r);
+    if (!qf || !kf) {
+        free(qf);
+        free(kf);
+        return -1;
+    }
+
+    for (int64_t t = 0; t < T; ++t) {
+        const double a = alpha ? alpha[t] : 1.0;
+        for (int32_t i = 0; i < r; ++i) {
+            qf[i] = apply_feature_map(q[t * r + i], phi_mode);
+            kf[i] = apply_feature_map(k[t * r + i], phi_mode);
+        }
+
+        /* write: S <- a*S + phi(k_t) v_t^T,  z <- a*z + phi(k_t) */
+        for (int32_t i = 0; i < r; ++i) {
+            for (int32_t j = 0; j < dv; ++j)
+                S[(int64_t)i * dv + j] = a * S[(int64_t)i * dv + j] + kf[i] * v[t * dv + j];
+            z[i] = a * z[i] + kf[i];
+        }
+
+        /* read: numerator phi(q_t)^T S_t, denominator phi(q_t)^T z_t + eps */
+        double d = 0.0;
+        for (int32_t i = 0; i < r; ++i)
+            d += qf[i] * z[i];
+        if (den)
+            den[t] = d;
+        for (int32_t j = 0; j < dv; ++j) {
+            double num = 0.0;
+            for (int32_t i = 0; i < r; ++i)
+                num += qf[i] * S[(int64_t)i * dv + j];
+            y[t * dv + j] = num / (d + eps);
+        }
+    }
+
+    free(qf);
+    free(kf);
+    return 0;
+}
