@@ -1,0 +1,147 @@
+/*
+ * linattn.h -- C ABI of the causal kernelized linear-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Linear attention：把历史写进状态", hs-black.github.io):
+ *   features      q~ = phi(q), k~ = phi(k), phi(x) = ELU(x)+1 = x+1 (x > 0), exp(x) (x <= 0)
+ *                 (section "关键改写：让求和先发生")
+ *   state write   S_t = alpha_t * S_{t-1} + k~_t v_t^T     S is r x dv, feature-major
+ *                 z_t = alpha_t * z_{t-1} + k~_t           z is r
+ *                 (sections "公式里的每个维度" and "加一个门"; alpha == 1 when ungated)
+ *   read-out      y_t = (q~_t^T S_t) / (q~_t^T z_t + eps)  -- the state is written
+ *                 first, so y_t includes token t; eps is added to the denominator,
+ *                 never max(den, eps) (sections "每来一个 token…" and "ε 是数值保护")
+ * Prefill evaluates this over a whole sequence chunk by chunk (section "一个 chunk
+ * 的输出由两部分组成"); decode applies one step per call (section "训练时，状态更新
+ * 也能按块并行": the token recurrence is the decode form).  Here the feature width r
+ * equals the key width d, since phi is elementwise.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers to dense, contiguous, row-major
+ *     arrays owned by the caller.  The library allocates nothing, keeps nothing
+ *     between calls and never synchronises: work is enqueued on `stream`
+ *     (a hipStream_t; NULL means the default stream) and the caller synchronises.
+ *   - Arguments are checked on the host before anything is enqueued.  On any
+ *     status other than LA_OK nothing has been launched and no output has been
+ *     written.  Faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - Outputs must not overlap inputs or each other (LA_ERR_ALIAS).
+ *   - dtypes: the io dtype (q, k, v and the output y) is LA_BF16, LA_F32 or
+ *     LA_F64.  The state dtype (S, z and the gate alpha) is LA_F32 for bf16 and
+ *     f32 io, LA_F64 for f64 io; any other pairing is LA_ERR_DTYPE.
+ *   - alpha, when given, must lie in [0, 1] (section "加一个门"); alpha = 0 resets
+ *     the state exactly.  Values outside [0, 1] are not checked and give
+ *     unspecified results.
+ *   - Calls are thread-safe; calls that share output buffers on concurrent
+ *     streams race.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+    LA_OK = 0,
+    LA_ERR_NULL = 1,        /* a required pointer is NULL */
+    LA_ERR_SHAPE = 2,       /* a size is < 1, or too large to index */
+    LA_ERR_DTYPE = 3,       /* unknown dtype, or an io/state pairing that is not allowed */
+    LA_ERR_EPS = 4,         /* eps is negative, NaN or infinite (0 is allowed) */
+    LA_ERR_CHUNK = 5,       /* chunk < 1 */
+    LA_ERR_UNSUPPORTED = 6, /* valid request with no kernel: d or dv > 128, chunk > 128 */
+    LA_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
+    LA_ERR_ALIAS = 8        /* an output overlaps an input or another output */
+} la_status;
+
+typedef enum la_dtype {
+    LA_F64 = 0,
+    LA_F32 = 1,
+    LA_BF16 = 2
+} la_dtype;
+
+/* Largest feature width d (= r), value width dv and chunk any kernel handles. */
+#define LA_MAX_WIDTH 128
+#define LA_MAX_CHUNK 128
+
+/*
+ * la_state_init -- S_0 = 0, z_0 = 0 for n_states independent states
+ * (section "每来一个 token，更新两个累加器": both accumulators start at zero).
+ *   S  [n_states, r, dv]  state_dtype, written
+ *   z  [n_states, r]      state_dtype, written
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE (n_states, r or dv < 1), LA_ERR_DTYPE
+ * (state_dtype not LA_F32/LA_F64), LA_ERR_ALIAS (S and z overlap), LA_ERR_LAUNCH.
+ * Enqueues a fill kernel (not a memset node), so it may be captured in a graph.
+ */
+la_status la_state_init(void *S, void *z, int64_t n_states, int32_t r, int32_t dv,
+                        la_dtype state_dtype, hipStream_t stream);
+
+/*
+ * la_prefill_chunked -- run B*H independent sequences of T tokens through the
+ * recurrence, continuing from the state in S and z, and return every output
+ * and the final state.  The work is organised chunk by chunk (section "一个 chunk
+ * 的输出由两部分组成"): for each chunk, the inter-chunk read Q~c S_prev and
+ * Q~c z_prev, the intra-chunk masked (Q~c K~c^T . M) Vc and its row sums, and the
+ * state write S_next = S_prev + K~c^T Vc, z_next = z_prev + sum of K~c rows; with a
+ * gate, the cumulative gate products inside the chunk weight the mask, the read
+ * of S_prev and the write.  `chunk` changes only the rounding, never the result.
+ *   Q, K   [B, H, T, d]   io_dtype, read
+ *   V      [B, H, T, dv]  io_dtype, read
+ *   alpha  [B, H, T]      state_dtype, read; NULL = ungated (alpha == 1)
+ *   Y      [B, H, T, dv]  io_dtype, written
+ *   S      [B, H, d, dv]  state_dtype, read (state before token 0) and overwritten
+ *                         with the state after token T-1
+ *   z      [B, H, d]      state_dtype, same as S
+ *   eps    >= 0, added to every denominator
+ *   chunk  tokens per chunk, 1..128 (the last chunk of a sequence may be shorter)
+ * bf16 io with d = dv = 128 and chunk 64 or 128 runs on bf16 MFMA with fp32
+ * accumulation and fp32 state; every other valid request runs a general kernel
+ * that computes in the state dtype.
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE (B, H, T, d, dv < 1), LA_ERR_DTYPE, LA_ERR_EPS,
+ * LA_ERR_CHUNK, LA_ERR_UNSUPPORTED (d or dv > 128, chunk > 128), LA_ERR_ALIAS,
+ * LA_ERR_LAUNCH.
+ */
+la_status la_prefill_chunked(const void *Q, const void *K, const void *V, const void *alpha,
+                             la_dtype io_dtype, int64_t B, int64_t H, int64_t T,
+                             int32_t d, int32_t dv, double eps, int32_t chunk,
+                             void *Y, void *S, void *z, la_dtype state_dtype,
+                             hipStream_t stream);
+
+/*
+ * la_decode_step -- one token for each of n_states independent states, updated in
+ * place: S <- alpha*S + k~ v^T, z <- alpha*z + k~, then y = q~^T S / (q~^T z + eps)
+ * (the minimal per-token loop of section "最小递推里，每一行都有张量意义", gated as
+ * in section "加一个门").  A state can be a (request, layer, head) slot of a batch.
+ *   q, k   [n_states, d]      io_dtype, read
+ *   v      [n_states, dv]     io_dtype, read
+ *   alpha  [n_states]         state_dtype, read; NULL = ungated
+ *   y      [n_states, dv]     io_dtype, written
+ *   S      [n_states, d, dv]  state_dtype, read and written in place
+ *   z      [n_states, d]      state_dtype, read and written in place
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_EPS,
+ * LA_ERR_UNSUPPORTED (d or dv > 128), LA_ERR_ALIAS, LA_ERR_LAUNCH.
+ */
+la_status la_decode_step(const void *q, const void *k, const void *v, const void *alpha,
+                         la_dtype io_dtype, int64_t n_states, int32_t d, int32_t dv,
+                         double eps, void *y, void *S, void *z, la_dtype state_dtype,
+                         hipStream_t stream);
+
+/* Static description of a status code; never NULL. */
+const char *la_status_str(la_status status);
+
+/*
+ * Which prefill kernel a request would run, without running it:
+ *   1 = bf16 MFMA chunked kernel, 0 = general kernel, -1 = the request is rejected
+ *   (the same checks as la_prefill_chunked on the scalar arguments).
+ */
+int32_t la_prefill_variant(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk,
+                           int32_t gated, la_dtype state_dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,509 @@
+// General kernels: state initialisation, the general chunked prefill (any d, dv <= 128,
+// chunk <= 128, f64/f32/bf16 io, arithmetic in the state dtype) and the batched
+// decode step.
+//
+// The operation is the one of page "Linear attention：把历史写进状态"
+// (hs-black.github.io): phi = ELU+1, gated write S = a*S + k~ v^T, z = a*z + k~, then
+// y = q~^T S / (q~^T z + eps).
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace la {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ===================================================================== state init
+// Zero fill in three parts so the bulk uses aligned 16-byte stores.
+__global__ __launch_bounds__(kThreads) void zero_fill_kernel(unsigned char *__restrict__ head, int64_t n_head,
+                                                             uint4 *__restrict__ bulk, int64_t n_bulk,
+                                                             unsigned char *__restrict__ tail, int64_t n_tail)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t i = i0; i < n_bulk; i += stride)
+        bulk[i] = zero;
+    for (int64_t i = i0; i < n_head; i += stride)
+        head[i] = 0;
+    for (int64_t i = i0; i < n_tail; i += stride)
+        tail[i] = 0;
+}
+
+hipError_t zero_fill(void *p, int64_t nbytes, hipStream_t stream)
+{
+    unsigned char *b = static_cast<unsigned char *>(p);
+    int64_t n_head = (int64_t)((16 - (reinterpret_cast<uintptr_t>(b) & 15)) & 15);
+    if (n_head > nbytes)
+        n_head = nbytes;
+    const int64_t n_bulk = (nbytes - n_head) / 16;
+    const int64_t n_tail = nbytes - n_head - n_bulk * 16;
+    int64_t work = n_bulk > n_head ? n_bulk : n_head;
+    if (n_tail > work)
+        work = n_tail;
+    int64_t blocks = (work + kThreads - 1) / kThreads;
+    if (blocks > 16384)
+        blocks = 16384;
+    if (blocks < 1)
+        blocks = 1;
+    zero_fill_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(
+        b, n_head, reinterpret_cast<uint4 *>(b + n_head), n_bulk, b + n_head + n_bulk * 16, n_tail);
+    return hipGetLastError();
+}
+
+// ===================================================================== general prefill
+constexpr int kRB = 16;        // query rows per block
+constexpr int kIB = 16;        // key tokens per block (kRB * kIB == kThreads)
+constexpr int kMaxSlice = 32;  // value columns per workgroup
+constexpr int kPairs = kRB * kMaxSlice / kThreads;
+constexpr int kStateRegs = LA_MAX_WIDTH * kMaxSlice / kThreads;
+static_assert(kRB * kIB == kThreads, "one score per thread");
+
+__device__ __forceinline__ float log_acc(float x) { return logf(x); }
+__device__ __forceinline__ double log_acc(double x) { return log(x); }
+__device__ __forceinline__ float exp_acc(float x) { return expf(x); }
+__device__ __forceinline__ double exp_acc(double x) { return exp(x); }
+
+template <typename TA>
+size_t general_prefill_lds_bytes(int d, int slice)
+{
+    const int dp = d + 1;
+    return sizeof(TA) * (size_t)(d * slice + d + kRB * dp + kIB * dp + kIB * slice + kRB * kIB +
+                                 LA_MAX_CHUNK + kRB + kIB) +
+           sizeof(int) * LA_MAX_CHUNK;
+}
+
+// One workgroup per (sequence, slice of value columns).  The sequence is walked
+// chunk by chunk; inside a chunk the outputs are produced kRB rows at a time from
+// the inter-chunk read of the previous state plus the masked intra-chunk scores,
+// then the chunk is written into the state.  Gates enter through the log-sum of
+// the gates since the last zero gate (lg) and the position of that zero gate (zp):
+// the product of gates over (i, j] is 0 when a zero gate lies in (i, j], else
+// exp(lg[j] - lg[i]).
+template <typename TI, typename TA>
+__global__ __launch_bounds__(kThreads) void prefill_general_kernel(
+    const TI *__restrict__ Q, const TI *__restrict__ K, const TI *__restrict__ V, const TA *__restrict__ alpha,
+    int64_t T, int d, int dv, int slice, TA eps, int chunk, TI *__restrict__ Y, TA *__restrict__ S,
+    TA *__restrict__ z)
+{
+    const int tid = threadIdx.x;
+    const int64_t h = blockIdx.x;
+    const int c0 = blockIdx.y * slice;
+    const int nc = min(slice, dv - c0);
+    const int dp = d + 1;  // padded row stride of the Q~ and K~ tiles
+
+    const TI *Qh = Q + h * T * d;
+    const TI *Kh = K + h * T * d;
+    const TI *Vh = V + h * T * dv;
+    const TA *Ah = alpha ? alpha + h * T : nullptr;
+    TI *Yh = Y + h * T * dv;
+    TA *Sh = S + h * (int64_t)d * dv;
+    TA *zh = z + h * d;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    TA *Ss = reinterpret_cast<TA *>(smem_raw);  // [d][slice] state slice
+    TA *zs = Ss + d * slice;                     // [d]
+    TA *Qt = zs + d;                             // [kRB][dp] phi(q) rows
+    TA *Kt = Qt + kRB * dp;                      // [kIB][dp] phi(k) rows
+    TA *Vt = Kt + kIB * dp;                      // [kIB][slice]
+    TA *At = Vt + kIB * slice;                   // [kRB][kIB] masked, gated scores
+    TA *lg = At + kRB * kIB;                     // [LA_MAX_CHUNK]
+    TA *den_s = lg + LA_MAX_CHUNK;               // [kRB]
+    TA *wk = den_s + kRB;                        // [kIB] weight of a write at the chunk end
+    int *zp = reinterpret_cast<int *>(wk + kIB); // [LA_MAX_CHUNK]
+
+    // product of the gates of tokens i+1..j of the chunk (i <= j)
+    auto pair_decay = [&](int j, int i) -> TA {
+        if (!Ah)
+            return TA(1);
+        if (zp[j] > i)
+            return TA(0);
+        return exp_acc(lg[j] - lg[i]);
+    };
+    // product of the gates of tokens 0..j of the chunk: what is left of the incoming state
+    auto start_decay = [&](int j) -> TA {
+        if (!Ah)
+            return TA(1);
+        if (zp[j] >= 0)
+            return TA(0);
+        return exp_acc(lg[j]);
+    };
+
+    for (int e = tid; e < d * nc; e += kThreads) {
+        const int f = e / nc, c = e - f * nc;
+        Ss[f * slice + c] = Sh[(int64_t)f * dv + c0 + c];
+    }
+    for (int f = tid; f < d; f += kThreads)
+        zs[f] = zh[f];
+    __syncthreads();
+
+    for (int64_t t0 = 0; t0 < T; t0 += chunk) {
+        const int n = (int)min((int64_t)chunk, T - t0);
+        if (Ah && tid == 0) {
+            TA acc = 0;
+            int last = -1;
+            for (int j = 0; j < n; ++j) {
+                const TA a = Ah[t0 + j];
+                if (a == TA(0)) {
+                    last = j;
+                    acc = TA(0);
+                } else {
+                    acc += log_acc(a);
+                }
+                lg[j] = acc;
+                zp[j] = last;
+            }
+        }
+
+        // ---------------- outputs of the chunk, kRB rows at a time
+        for (int j0 = 0; j0 < n; j0 += kRB) {
+            const int rb = min(kRB, n - j0);
+            for (int e = tid; e < rb * d; e += kThreads) {
+                const int jj = e / d, f = e - jj * d;
+                Qt[jj * dp + f] = phi_accurate(to_acc<TA>(Qh[(t0 + j0 + jj) * d + f]));
+            }
+            __syncthreads();
+
+            // inter-chunk read: what is left of the previous state, seen by q~
+            TA num[kPairs];
+#pragma unroll
+            for (int p = 0; p < kPairs; ++p) {
+                num[p] = TA(0);
+                const int e = tid + p * kThreads, jj = e / slice, c = e - jj * slice;
+                if (jj < rb && c < nc) {
+                    TA acc = 0;
+                    for (int f = 0; f < d; ++f)
+                        acc += Qt[jj * dp + f] * Ss[f * slice + c];
+                    num[p] = start_decay(j0 + jj) * acc;
+                }
+            }
+            if (tid < rb) {
+                TA acc = 0;
+                for (int f = 0; f < d; ++f)
+                    acc += Qt[tid * dp + f] * zs[f];
+                den_s[tid] = start_decay(j0 + tid) * acc;
+            }
+
+            // intra-chunk part: scores masked to i <= j and weighted by the gates
+            const int jmax = j0 + rb - 1;
+            for (int i0 = 0; i0 <= jmax; i0 += kIB) {
+                const int ib = min(kIB, n - i0);
+                __syncthreads();
+                for (int e = tid; e < ib * d; e += kThreads) {
+                    const int ii = e / d, f = e - ii * d;
+                    Kt[ii * dp + f] = phi_accurate(to_acc<TA>(Kh[(t0 + i0 + ii) * d + f]));
+                }
+                for (int e = tid; e < ib * nc; e += kThreads) {
+                    const int ii = e / nc, c = e - ii * nc;
+                    Vt[ii * slice + c] = to_acc<TA>(Vh[(t0 + i0 + ii) * dv + c0 + c]);
+                }
+                __syncthreads();
+                {
+                    const int jj = tid / kIB, ii = tid - jj * kIB;
+                    const int j = j0 + jj, i = i0 + ii;
+                    TA a = TA(0);
+                    if (jj < rb && ii < ib && i <= j) {
+                        TA acc = 0;
+                        for (int f = 0; f < d; ++f)
+                            acc += Qt[jj * dp + f] * Kt[ii * dp + f];
+                        a = acc * pair_decay(j, i);
+                    }
+                    At[jj * kIB + ii] = a;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int p = 0; p < kPairs; ++p) {
+                    const int e = tid + p * kThreads, jj = e / slice, c = e - jj * slice;
+                    if (jj < rb && c < nc) {
+                        TA acc = 0;
+                        for (int ii = 0; ii < ib; ++ii)
+                            acc += At[jj * kIB + ii] * Vt[ii * slice + c];
+                        num[p] += acc;
+                    }
+                }
+                if (tid < rb) {
+                    TA acc = 0;
+                    for (int ii = 0; ii < ib; ++ii)
+                        acc += At[tid * kIB + ii];
+                    den_s[tid] += acc;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < kPairs; ++p) {
+                const int e = tid + p * kThreads, jj = e / slice, c = e - jj * slice;
+                if (jj < rb && c < nc)
+                    Yh[(t0 + j0 + jj) * dv + c0 + c] = from_acc<TI>(num[p] / (den_s[jj] + eps));
+            }
+            __syncthreads();
+        }
+
+        // ---------------- write the chunk into the state
+        const TA g_end = start_decay(n - 1);
+        TA sreg[kStateRegs];
+#pragma unroll
+        for (int p = 0; p < kStateRegs; ++p) {
+            const int e = tid + p * kThreads;
+            sreg[p] = TA(0);
+            if (e < d * nc) {
+                const int f = e / nc, c = e - f * nc;
+                sreg[p] = g_end * Ss[f * slice + c];
+            }
+        }
+        TA zreg = tid < d ? g_end * zs[tid] : TA(0);
+        for (int i0 = 0; i0 < n; i0 += kIB) {
+            const int ib = min(kIB, n - i0);
+            __syncthreads();
+            for (int e = tid; e < ib * d; e += kThreads) {
+                const int ii = e / d, f = e - ii * d;
+                Kt[ii * dp + f] = phi_accurate(to_acc<TA>(Kh[(t0 + i0 + ii) * d + f]));
+            }
+            for (int e = tid; e < ib * nc; e += kThreads) {
+                const int ii = e / nc, c = e - ii * nc;
+                Vt[ii * slice + c] = to_acc<TA>(Vh[(t0 + i0 + ii) * dv + c0 + c]);
+            }
+            if (tid < ib)
+                wk[tid] = pair_decay(n - 1, i0 + tid);
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < kStateRegs; ++p) {
+                const int e = tid + p * kThreads;
+                if (e < d * nc) {
+                    const int f = e / nc, c = e - f * nc;
+                    TA acc = 0;
+                    for (int ii = 0; ii < ib; ++ii)
+                        acc += (wk[ii] * Kt[ii * dp + f]) * Vt[ii * slice + c];
+                    sreg[p] += acc;
+                }
+            }
+            if (tid < d) {
+                TA acc = 0;
+                for (int ii = 0; ii < ib; ++ii)
+                    acc += wk[ii] * Kt[ii * dp + tid];
+                zreg += acc;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < kStateRegs; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < d * nc) {
+                const int f = e / nc, c = e - f * nc;
+                Ss[f * slice + c] = sreg[p];
+            }
+        }
+        if (tid < d)
+            zs[tid] = zreg;
+        __syncthreads();
+    }
+
+    for (int e = tid; e < d * nc; e += kThreads) {
+        const int f = e / nc, c = e - f * nc;
+        Sh[(int64_t)f * dv + c0 + c] = Ss[f * slice + c];
+    }
+    if (blockIdx.y == 0)
+        for (int f = tid; f < d; f += kThreads)
+            zh[f] = zs[f];
+}
+
+template <typename TI, typename TA>
+hipError_t launch_general_typed(const PrefillArgs &a, hipStream_t stream)
+{
+    // widest value slice whose working set fits a 64 KiB LDS budget
+    int slice = a.dv < kMaxSlice ? a.dv : kMaxSlice;
+    while (slice > 1 && general_prefill_lds_bytes<TA>(a.d, slice) > 65536)
+        slice /= 2;
+    const size_t lds = general_prefill_lds_bytes<TA>(a.d, slice);
+    const unsigned n_slices = (unsigned)((a.dv + slice - 1) / slice);
+    prefill_general_kernel<TI, TA><<<dim3((unsigned)a.n_heads, n_slices), dim3(kThreads), lds, stream>>>(
+        static_cast<const TI *>(a.Q), static_cast<const TI *>(a.K), static_cast<const TI *>(a.V),
+        static_cast<const TA *>(a.alpha), a.T, a.d, a.dv, slice, static_cast<TA>(a.eps), a.chunk,
+        static_cast<TI *>(a.Y), static_cast<TA *>(a.S), static_cast<TA *>(a.z));
+    return hipGetLastError();
+}
+
+// ===================================================================== decode
+// d = dv = 128: one workgroup of 256 threads per state.  Thread (rg, cg) owns
+// VEC consecutive columns (cg) of the rows rg, rg + NRG, ..., so each wave reads
+// adjacent full rows; all of a thread's rows are loaded before any is used.
+template <typename TI, typename TA, int VEC>
+__global__ __launch_bounds__(kThreads) void decode_w128_kernel(
+    const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v, const TA *__restrict__ alpha,
+    TA eps, TI *__restrict__ y, TA *__restrict__ S, TA *__restrict__ z)
+{
+    constexpr int D = 128, DV = 128, NCG = DV / VEC, NRG = kThreads / NCG, ROWS = D / NRG;
+    typedef TA vec_t __attribute__((ext_vector_type(VEC)));
+    __shared__ TA kf[D], qf[D], vs[DV];
+    __shared__ TA red[NRG][DV];
+    __shared__ TA dred[kThreads / 64];
+
+    const int tid = threadIdx.x;
+    const int64_t n = blockIdx.x;
+    const int cg = tid % NCG, rg = tid / NCG;
+    vec_t *Sv = reinterpret_cast<vec_t *>(S + n * (int64_t)(D * DV));
+
+    vec_t s[ROWS];
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i)
+        s[i] = Sv[(rg + i * NRG) * NCG + cg];
+    const TA zf = tid < D ? z[n * D + tid] : TA(0);
+    if (tid < D) {
+        kf[tid] = phi_accurate(to_acc<TA>(k[n * D + tid]));
+        qf[tid] = phi_accurate(to_acc<TA>(q[n * D + tid]));
+        vs[tid] = to_acc<TA>(v[n * DV + tid]);
+    }
+    const TA a = alpha ? alpha[n] : TA(1);
+    __syncthreads();
+
+    TA part[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        part[e] = TA(0);
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int f = rg + i * NRG;
+        const TA kv = kf[f], qv = qf[f];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            s[i][e] = a * s[i][e] + kv * vs[cg * VEC + e];
+            part[e] += qv * s[i][e];
+        }
+        Sv[f * NCG + cg] = s[i];
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        red[rg][cg * VEC + e] = part[e];
+
+    TA dpart = TA(0);
+    if (tid < D) {
+        const TA zn = a * zf + kf[tid];
+        z[n * D + tid] = zn;
+        dpart = qf[tid] * zn;
+    }
+    dpart = wave_sum(dpart);
+    if ((tid & 63) == 0)
+        dred[tid >> 6] = dpart;
+    __syncthreads();
+    if (tid < DV) {
+        TA num = TA(0);
+#pragma unroll
+        for (int r = 0; r < NRG; ++r)
+            num += red[r][tid];
+        TA den = TA(0);
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w)
+            den += dred[w];
+        y[n * DV + tid] = from_acc<TI>(num / (den + eps));
+    }
+}
+
+// Any d, dv <= 128: thread (rg, c) owns column c of rows rg, rg + nrg, ...
+template <typename TI, typename TA>
+__global__ __launch_bounds__(kThreads) void decode_general_kernel(
+    const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v, const TA *__restrict__ alpha,
+    int d, int dv, TA eps, TI *__restrict__ y, TA *__restrict__ S, TA *__restrict__ z)
+{
+    __shared__ TA kf[LA_MAX_WIDTH], qf[LA_MAX_WIDTH], vs[LA_MAX_WIDTH];
+    __shared__ TA red[kThreads];
+    __shared__ TA dred[kThreads / 64];
+    const int tid = threadIdx.x;
+    const int64_t n = blockIdx.x;
+    if (tid < d) {
+        kf[tid] = phi_accurate(to_acc<TA>(k[n * d + tid]));
+        qf[tid] = phi_accurate(to_acc<TA>(q[n * d + tid]));
+    }
+    if (tid < dv)
+        vs[tid] = to_acc<TA>(v[n * dv + tid]);
+    const TA a = alpha ? alpha[n] : TA(1);
+    __syncthreads();
+
+    const int nrg = kThreads / dv;
+    const int c = tid % dv, rg = tid / dv;
+    TA *Sn = S + n * (int64_t)d * dv;
+    TA part = TA(0);
+    if (rg < nrg) {
+        for (int f = rg; f < d; f += nrg) {
+            const TA s = a * Sn[(int64_t)f * dv + c] + kf[f] * vs[c];
+            Sn[(int64_t)f * dv + c] = s;
+            part += qf[f] * s;
+        }
+    }
+    red[tid] = part;
+    TA dpart = TA(0);
+    if (tid < d) {
+        const TA zn = a * z[n * d + tid] + kf[tid];
+        z[n * d + tid] = zn;
+        dpart = qf[tid] * zn;
+    }
+    dpart = wave_sum(dpart);
+    if ((tid & 63) == 0)
+        dred[tid >> 6] = dpart;
+    __syncthreads();
+    if (tid < dv) {
+        TA num = TA(0);
+        for (int r = 0; r < nrg; ++r)
+            num += red[r * dv + tid];
+        TA den = TA(0);
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w)
+            den += dred[w];
+        y[n * dv + tid] = from_acc<TI>(num / (den + eps));
+    }
+}
+
+template <typename TI, typename TA>
+hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t stream)
+{
+    constexpr int VEC = 16 / sizeof(TA);
+    const bool aligned = (reinterpret_cast<uintptr_t>(a.S) % 16) == 0;
+    if (a.d == 128 && a.dv == 128 && aligned) {
+        decode_w128_kernel<TI, TA, VEC><<<dim3((unsigned)a.n_states), dim3(kThreads), 0, stream>>>(
+            static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
+            static_cast<const TA *>(a.alpha), static_cast<TA>(a.eps), static_cast<TI *>(a.y),
+            static_cast<TA *>(a.S), static_cast<TA *>(a.z));
+    } else {
+        decode_general_kernel<TI, TA><<<dim3((unsigned)a.n_states), dim3(kThreads), 0, stream>>>(
+            static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
+            static_cast<const TA *>(a.alpha), a.d, a.dv, static_cast<TA>(a.eps), static_cast<TI *>(a.y),
+            static_cast<TA *>(a.S), static_cast<TA *>(a.z));
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_state_init(void *S, void *z, int64_t n_states, int32_t r, int32_t dv, la_dtype state_dtype,
+                             hipStream_t stream)
+{
+    const int64_t es = state_dtype == LA_F64 ? 8 : 4;
+    hipError_t e = zero_fill(S, n_states * r * dv * es, stream);
+    if (e != hipSuccess)
+        return e;
+    return zero_fill(z, n_states * r * es, stream);
+}
+
+hipError_t launch_prefill_general(const PrefillArgs &a, la_dtype io_dtype, hipStream_t stream)
+{
+    switch (io_dtype) {
+    case LA_F64:
+        return launch_general_typed<double, double>(a, stream);
+    case LA_F32:
+        return launch_general_typed<float, float>(a, stream);
+    default:
+        return launch_general_typed<bf16, float>(a, stream);
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, la_dtype io_dtype, hipStream_t stream)
+{
+    switch (io_dtype) {
+    case LA_F64:
+        return launch_decode_typed<double, double>(a, stream);
+    case LA_F32:
+        return launch_decode_typed<float, float>(a, stream);
+    default:
+        return launch_decode_typed<bf16, float>(a, stream);
+    }
+}
+
+}  // namespace la

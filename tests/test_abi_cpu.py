@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status codes
+before anything is launched (so no call here reaches the device)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import recurrent_state_chunkwise_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+OK, NULL, SHAPE, DTYPE, EPS, CHUNK, UNSUP, LAUNCH, ALIAS = range(9)
+F64, F32, BF16 = la.LA_F64, la.LA_F32, la.LA_BF16
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(la.library_path()):
+        from recurrent_state_chunkwise_amd import build
+        build.build()
+    return la.library()
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = _declared_functions()
+    assert set(names) >= {"la_state_init", "la_prefill_chunked", "la_decode_step", "la_status_str",
+                          "la_prefill_variant"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = la.la_status_str(code)
+        assert isinstance(s, str) and s
+    assert la.la_status_str(0) == "ok"
+    assert la.la_status_str(99) == "unknown status"
+
+
+# fake, distinct, non-overlapping device addresses: validation fails before any use
+P = [ctypes.c_void_p(0x100000000 + i * 0x10000000) for i in range(8)]
+
+
+def prefill(lib, Q=P[0], K=P[1], V=P[2], alpha=None, io=BF16, B=1, H=1, T=8, d=4, dv=4, eps=1e-6, chunk=4,
+            Y=P[3], S=P[4], z=P[5], st=F32):
+    return lib.la_prefill_chunked(Q, K, V, alpha, io, B, H, T, d, dv, eps, chunk, Y, S, z, st, None)
+
+
+def decode(lib, q=P[0], k=P[1], v=P[2], alpha=None, io=BF16, N=4, d=4, dv=4, eps=1e-6, y=P[3], S=P[4],
+           z=P[5], st=F32):
+    return lib.la_decode_step(q, k, v, alpha, io, N, d, dv, eps, y, S, z, st, None)
+
+
+def test_prefill_rejections(lib):
+    assert prefill(lib, Q=None) == NULL
+    assert prefill(lib, Y=None) == NULL
+    assert prefill(lib, z=None) == NULL
+    assert prefill(lib, T=0) == SHAPE            # empty sequence (ch. 45 input contract)
+    assert prefill(lib, B=0) == SHAPE
+    assert prefill(lib, H=-1) == SHAPE
+    assert prefill(lib, d=0) == SHAPE
+    assert prefill(lib, dv=0) == SHAPE
+    assert prefill(lib, io=7) == DTYPE
+    assert prefill(lib, io=BF16, st=F64) == DTYPE
+    assert prefill(lib, io=F64, st=F32) == DTYPE
+    assert prefill(lib, io=F32, st=BF16) == DTYPE
+    assert prefill(lib, eps=-1e-9) == EPS
+    assert prefill(lib, eps=math.nan) == EPS
+    assert prefill(lib, eps=math.inf) == EPS
+    assert prefill(lib, chunk=0) == CHUNK
+    assert prefill(lib, chunk=129) == UNSUP
+    assert prefill(lib, d=129) == UNSUP
+    assert prefill(lib, dv=256) == UNSUP
+    assert prefill(lib, B=1 << 40, H=1 << 40) == SHAPE
+    # outputs overlapping inputs or each other
+    assert prefill(lib, Y=P[0]) == ALIAS
+    assert prefill(lib, S=ctypes.c_void_p(P[2].value + 8)) == ALIAS
+    assert prefill(lib, z=P[4]) == ALIAS
+    assert prefill(lib, alpha=P[4]) == ALIAS
+
+
+def test_decode_rejections(lib):
+    assert decode(lib, q=None) == NULL
+    assert decode(lib, S=None) == NULL
+    assert decode(lib, N=0) == SHAPE
+    assert decode(lib, N=1 << 33) == SHAPE
+    assert decode(lib, d=0) == SHAPE
+    assert decode(lib, io=BF16, st=F64) == DTYPE
+    assert decode(lib, eps=-1.0) == EPS
+    assert decode(lib, d=200) == UNSUP
+    assert decode(lib, y=P[1]) == ALIAS
+    assert decode(lib, S=P[5]) == ALIAS
+    assert decode(lib, alpha=P[3]) == ALIAS
+
+
+def test_state_init_rejections(lib):
+    assert lib.la_state_init(None, P[1], 1, 4, 4, F32, None) == NULL
+    assert lib.la_state_init(P[0], P[1], 0, 4, 4, F32, None) == SHAPE
+    assert lib.la_state_init(P[0], P[1], 1, 4, 4, BF16, None) == DTYPE
+    assert lib.la_state_init(P[0], P[0], 1, 4, 4, F32, None) == ALIAS
+
+
+def test_prefill_variant(lib):
+    assert la.la_prefill_variant(BF16, 16, 16, 16, False, F32) == 0
+    assert la.la_prefill_variant(F64, 16, 16, 16, False, F64) == 0
+    assert la.la_prefill_variant(F32, 128, 128, 64, True, F32) == 0
+    assert la.la_prefill_variant(BF16, 129, 128, 64, False, F32) == -1
+    assert la.la_prefill_variant(BF16, 128, 128, 0, False, F32) == -1
+    assert la.la_prefill_variant(BF16, 128, 128, 64, False, F64) == -1
+
+
+def test_binding_shape_contract_cpu():
+    """The binding rejects Q/K width mismatches and empty sequences (ValueError,
+    the first page's convention) before touching any device."""
+    import torch
+    q = torch.zeros(1, 1, 2, 2)
+    with pytest.raises(ValueError):
+        la.la_prefill_chunked(q, torch.zeros(1, 1, 2, 3), torch.zeros(1, 1, 2, 1), None, 1e-6, 4,
+                              torch.zeros(1, 1, 2, 1), torch.zeros(1, 1, 2, 1), torch.zeros(1, 1, 2))
+    e = torch.zeros(1, 1, 0, 2)
+    with pytest.raises(ValueError):
+        la.la_prefill_chunked(e, e, torch.zeros(1, 1, 0, 1), None, 1e-6, 4, torch.zeros(1, 1, 0, 1),
+                              torch.zeros(1, 1, 2, 1), torch.zeros(1, 1, 2))
+    with pytest.raises(ValueError):
+        la.la_decode_step(torch.zeros(2, 3), torch.zeros(2, 4), torch.zeros(2, 1), None, 1e-6,
+                          torch.zeros(2, 1), torch.zeros(2, 3, 1), torch.zeros(2, 3))
