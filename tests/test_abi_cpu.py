@@ -114,6 +114,10 @@ def test_prefill_variant(lib):
     assert la.la_prefill_variant(BF16, 16, 16, 16, False, F32) == 0
     assert la.la_prefill_variant(F64, 16, 16, 16, False, F64) == 0
     assert la.la_prefill_variant(F32, 128, 128, 64, True, F32) == 0
+    assert la.la_prefill_variant(BF16, 128, 128, 64, False, F32) == 1
+    assert la.la_prefill_variant(BF16, 128, 128, 128, True, F32) == 1
+    assert la.la_prefill_variant(BF16, 128, 128, 32, True, F32) == 0
+    assert la.la_prefill_variant(BF16, 64, 128, 64, True, F32) == 0
     assert la.la_prefill_variant(BF16, 129, 128, 64, False, F32) == -1
     assert la.la_prefill_variant(BF16, 128, 128, 0, False, F32) == -1
     assert la.la_prefill_variant(BF16, 128, 128, 64, False, F64) == -1
