@@ -1,0 +1,229 @@
+"""Benchmark of the linear-attention hot path on one MI355X.
+
+One step = one state initialisation plus one la_prefill_chunked call over the
+ungated prefill workload B=4, H=16, T=4096, d=dv=128, chunk 64, bf16 inputs
+resident in HBM (the workload the prefill metric is quoted on).  `value` is
+whole-job prefill throughput in tokens/s (B*T tokens per step).  The same JSON
+line also carries:
+  roofline      the timed prefill call against the HBM roofline (algorithmic bytes:
+                Q, K, V read and Y written in bf16, 1,024 B per head-token, plus the
+                fp32 state read and written, 2 x 66,048 B per head), and its useful
+                MFMA flops against the bf16 dense peak;
+  decode        the batched decode workload (65,536 fp32 states seeded by 256
+                writes, 1,024 sequential steps) in state-steps/s with its HBM roofline
+                (133,120 B per state-step);
+  other         the gated prefill workloads, timed the same way;
+  cpu_baseline  the FP64 oracle timed on this host's cores on a sample of the
+                prefill workload.
+Run: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+STATE_BYTES = 128 * 128 * 4 + 128 * 4
+
+
+def prefill_bytes(B, H, T, gated):
+    return B * H * T * (1024 + (4 if gated else 0)) + 2 * B * H * STATE_BYTES
+
+
+def prefill_useful_flops(B, H, T, C, d=128, dv=128):
+    # per head-token: causal intra-chunk scores and A V ((C+1)(d+dv)), inter-chunk read
+    # and state write (4 d dv)
+    return B * H * T * ((C + 1) * (d + dv) + 4 * d * dv)
+
+
+def time_prefill(torch, la, wl, cfg, steps, warmup):
+    Q, K, V, A = wl.prefill_inputs(cfg, "cuda")
+    Y = torch.empty_like(V)
+    S = torch.empty((cfg.B, cfg.H, cfg.d, cfg.dv), device="cuda")
+    z = torch.empty((cfg.B, cfg.H, cfg.d), device="cuda")
+
+    def step():
+        la.la_state_init(S, z)
+        la.la_prefill_chunked(Q, K, V, A, cfg.eps, cfg.chunk, Y, S, z)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        la.la_state_init(S, z)
+        ev[i][0].record()
+        la.la_prefill_chunked(Q, K, V, A, cfg.eps, cfg.chunk, Y, S, z)
+        ev[i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    del Q, K, V, A, Y, S, z
+    return total_ms, call_ms, wall
+
+
+def time_decode(torch, la, wl, cfg, warmup=10):
+    N = cfg.n_states
+    # seed every state with 256 writes through the prefill path (untimed)
+    ks, vs = wl.decode_seed_inputs(cfg, "cuda")
+    S = torch.empty((N, 1, cfg.d, cfg.dv), device="cuda")
+    z = torch.empty((N, 1, cfg.d), device="cuda")
+    la.la_state_init(S, z)
+    Ys = torch.empty_like(vs)
+    la.la_prefill_chunked(ks, ks, vs, None, cfg.eps, 64, Ys, S, z)
+    del ks, vs, Ys
+    S, z = S.view(N, cfg.d, cfg.dv), z.view(N, cfg.d)
+    steps = cfg.steps
+    inputs = [wl.decode_step_inputs(cfg, i, "cuda") for i in range(steps)]
+    y = torch.empty((N, cfg.dv), device="cuda", dtype=torch.bfloat16)
+    Sw, zw = S.clone(), z.clone()
+    for i in range(warmup):  # on a scratch copy of the state
+        q, k, v = inputs[i]
+        la.la_decode_step(q, k, v, None, cfg.eps, y, Sw, zw)
+    del Sw, zw
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        q, k, v = inputs[i]
+        ev[i][0].record()
+        la.la_decode_step(q, k, v, None, cfg.eps, y, S, z)
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    del inputs, S, z, y
+    return total_ms, call_ms
+
+
+def cpu_baseline(wl, torch):
+    """The FP64 oracle on this host's cores, on a sample of the prefill workload."""
+    import oracle
+    import numpy as np
+    cfg = wl.PREFILL_UNGATED
+    threads = min(16, len(os.sched_getaffinity(0)))  # one GPU's share of the host
+    heads = cfg.B * cfg.H                             # the whole workload, ~15 CPU-seconds
+    Q, K, V, _ = wl.prefill_inputs(cfg, "cpu", B=1, H=heads)
+    f64 = lambda t: t.to(torch.float64).numpy()
+    q, k, v = f64(Q), f64(K), f64(V)
+    t0 = time.perf_counter()
+    oracle.recurrence_heads(q, k, v, eps=cfg.eps, threads=threads)
+    dt = time.perf_counter() - t0
+    head_tokens = heads * cfg.T
+    return {
+        "value": head_tokens / dt / cfg.H,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "all %d heads x %d tokens of the B=%d,H=%d,T=%d ungated workload (%.1f s wall, "
+                  "inputs drawn on the host); tokens/s = head-tokens/s / H" % (heads, cfg.T, cfg.B, cfg.H, cfg.T, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the decode and gated workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the data-parallel step shards by sequence with no communication); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import recurrent_state_chunkwise_amd as la
+    from recurrent_state_chunkwise_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    la.library()
+    cfg = wl.PREFILL_UNGATED
+    torch.cuda.synchronize()
+    total_ms, call_ms, wall = time_prefill(torch, la, wl, cfg, args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    tokens = cfg.B * cfg.T
+    value = tokens * args.steps / (total_ms / 1e3)
+    nbytes = prefill_bytes(cfg.B, cfg.H, cfg.T, cfg.gated)
+    flops = prefill_useful_flops(cfg.B, cfg.H, cfg.T, cfg.chunk)
+    achieved = nbytes / (call_ms / 1e3) / 1e9
+    out = {
+        "metric": "prefill tokens/s + %MFMA peak; decode state-steps/s + %HBM GB/s",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "T": cfg.T, "d": cfg.d, "dv": cfg.dv,
+                   "chunk": cfg.chunk, "gated": cfg.gated, "eps": cfg.eps, "state": "fp32",
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "kernel": "la_prefill_chunked (segment maps + scan + chunked prefill)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "call_ms": call_ms,
+            "algorithmic_bytes": nbytes,
+            "useful_mfma_tflops": flops / (call_ms / 1e3) / 1e12,
+            "mfma_frac": flops / (call_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+        },
+    }
+    if not args.no_extra:
+        dcfg = wl.DECODE
+        d_total, d_call = time_decode(torch, la, wl, dcfg)
+        d_bytes = dcfg.n_states * (2 * STATE_BYTES + 3 * 256 + 256)
+        out["decode"] = {
+            "workload": dcfg.name, "steps": dcfg.steps,
+            "value": dcfg.n_states * dcfg.steps / (d_total / 1e3), "unit": "state-steps/s",
+            "ms_per_step": d_total / dcfg.steps,
+            "roofline": {"kernel": "la_decode_step", "bound": "hbm",
+                         "achieved": d_bytes / (d_call / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": d_bytes / (d_call / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                         "call_ms": d_call, "algorithmic_bytes": d_bytes},
+        }
+        other = []
+        for ocfg in (wl.PREFILL_GATED, wl.PREFILL_LONG):
+            steps = 10 if ocfg.T <= 16384 else 3
+            o_total, o_call, _ = time_prefill(torch, la, wl, ocfg, steps, 2)
+            ob = prefill_bytes(ocfg.B, ocfg.H, ocfg.T, ocfg.gated)
+            of = prefill_useful_flops(ocfg.B, ocfg.H, ocfg.T, ocfg.chunk)
+            other.append({"workload": ocfg.name, "value": ocfg.B * ocfg.T / (o_call / 1e3), "unit": "tokens/s",
+                          "call_ms": o_call, "hbm_frac": ob / (o_call / 1e3) / 1e9 / HBM_PEAK_GBS,
+                          "mfma_frac": of / (o_call / 1e3) / 1e12 / BF16_PEAK_TFLOPS})
+        out["other"] = other
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
