@@ -49,6 +49,14 @@ constexpr int kD = 128;          // feature width d = r and value width dv
 constexpr int kThreads = 512;    // 8 waves
 constexpr float kLog2e = 1.4426950408889634f;
 
+// (sequence, segment) workgroups aimed for, per chunk size: one or two per compute unit
+#ifndef LA_SEGMENT_TARGET_C64
+#define LA_SEGMENT_TARGET_C64 256
+#endif
+#ifndef LA_SEGMENT_TARGET_C128
+#define LA_SEGMENT_TARGET_C128 256
+#endif
+
 // per-(sequence, segment) slot in Y: S [128][128], z [128], segment gate product, pad
 constexpr int kSlotFloats = kD * kD + kD + 4;
 constexpr int64_t kMinSegTokens = (kSlotFloats * 4 + kD * 2 - 1) / (kD * 2);
@@ -69,10 +77,11 @@ __device__ __forceinline__ void unpack8(uint4 u, float *f)
     }
 }
 
-// phi = ELU + 1 on the hardware exp2
+// phi = ELU + 1 as the median of (x + 1, e^x, 1): x + 1 for x > 0 (where e^x > x + 1 > 1)
+// and e^x for x <= 0 (where x + 1 <= e^x <= 1); e^x on the hardware exp2
 __device__ __forceinline__ float phi(float x)
 {
-    return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * kLog2e);
+    return __builtin_amdgcn_fmed3f(x + 1.f, __builtin_amdgcn_exp2f(x * kLog2e), 1.f);
 }
 
 // Buffer resources (gfx9 raw buffers): an access at or past num_records bytes reads
@@ -104,31 +113,54 @@ struct Cfg {
 // (KwT: features x tokens, VT: values x tokens) are the K-contiguous operands of the
 // contractions over tokens.  16-byte granules are XOR-swizzled per row so that the
 // 16 rows read by one MFMA operand land in distinct banks.
-template <int C>
+template <int C, bool SUMMARY>
 struct alignas(16) Smem {
     typedef Cfg<C> G;
-    alignas(16) bf16 Qs[C * kD];
-    alignas(16) bf16 Ks[C * kD];
-    alignas(16) bf16 KwT[kD * C];
-    alignas(16) bf16 VT[kD * C];
-    alignas(16) uint2 P[G::NPT * 64];   // bf16 A tiles, one 4-value group per lane
-    alignas(16) float rs[G::NPT * 16];  // row sums of each A tile
-    alignas(16) float zpart[8 * kD];    // per-wave partial sums of w phi(k)
+    static constexpr int QN = SUMMARY ? 1 : C * kD;
+    static constexpr int PN = SUMMARY ? 1 : G::NPT;
+    alignas(16) bf16 Qs[1][QN];             // phi(q) rows
+    alignas(16) bf16 Ks[1][QN];             // phi(k) rows; after the scores, output staging
+    alignas(16) bf16 KwT[1][kD * C];
+    alignas(16) bf16 VT[1][kD * C];
+    alignas(16) uint2 P[PN * 64];           // bf16 A tiles, one 4-value group per lane
+    alignas(16) float rs[PN * 16];          // row sums of each A tile
+    alignas(16) float zpart[1][8 * kD];     // per-wave partial sums of w phi(k)
     alignas(16) float zs[kD];
-    alignas(16) float den_q[C];         // phi(q_j) . z_prev
-    alignas(16) float inv_den[C];       // 1 / (denominator + eps)
-    alignas(16) float lg[2][C];         // in-chunk prefix sum of log(alpha) (0 at zero gates)
-    alignas(16) float gj[2][C];         // product of the chunk's gates up to j
-    alignas(16) int zp[2][C];           // last zero gate at or before j, -1 if none
+    alignas(16) float den_q[1][C];          // phi(q_j) . z_prev
+    alignas(16) float ivd[C];               // 1 / (denominator + eps)
+    alignas(16) float lg[2][C];             // in-chunk prefix sum of log(alpha) (0 at zero gates)
+    alignas(16) float gj[2][C];             // product of the chunk's gates up to j
+    alignas(16) int zp[2][C];               // last zero gate at or before j, -1 if none
 };
 
+// Sum over the 16 lanes of a DPP row, result in every lane of the row.
+__device__ __forceinline__ float row_sum16(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));  // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false));  // row_ror:2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false));  // row_ror:1
+    return v;
+}
+// v[l] + v[l ^ 16] and v[l] + v[l ^ 32] with the gfx950 lane-swap instructions
+__device__ __forceinline__ float xor16_sum(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // swizzled element offsets
-__device__ __forceinline__ int qk_off(int row, int col)  // [C][128], col multiple of 4
+__device__ __forceinline__ int qk_off(int row, int col)  // [C][128]
 {
     return row * kD + ((((col >> 3) ^ (row & 15)) << 3) | (col & 7));
 }
 template <int C>
-__device__ __forceinline__ int tm_off(int row, int tok)  // [128][C], tok multiple of 4
+__device__ __forceinline__ int tm_off(int row, int tok)  // [128][C]
 {
     int h;
     if constexpr (C == 128)
@@ -160,7 +192,7 @@ template <int C, bool GATED, bool SUMMARY>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 {
     typedef Cfg<C> G;
-    __shared__ Smem<C> sm;
+    __shared__ Smem<C, SUMMARY> sm;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -176,6 +208,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
     const int64_t s1 = seg == a.nseg - 1 ? a.T : s0 + a.seg_len;
     const int64_t len = s1 - s0;
     const int n_chunks = (int)((len + C - 1) / C);
+    auto chunk_len = [&](int c) { return (int)min((int64_t)C, len - (int64_t)c * C); };
 
     // this segment's rows of Q, K, V, Y (256 bytes per token) and of alpha (4 bytes)
     const int64_t row0 = head * a.T + s0;
@@ -208,23 +241,30 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
     }
     float g_seg = 1.f;  // product of all gates of the segment (SUMMARY)
 
-    // ---------------------------------------------------------------- staging roles
+    // ---------------------------------------------------------------- loads
     // every thread stages TPT consecutive tokens of one 8-wide granule of Q, K and V:
     // thread (fg, tg) holds granule fg of tokens tg*TPT .. tg*TPT + TPT - 1
     const int fg = tid & 15, tg = tid >> 4;
     uint4 raw_q[G::TPT], raw_k[G::TPT], raw_v[G::TPT];
     float araw[C / 64];
-
     const int ld_off = (tg * G::TPT) * kD * 2 + fg * 16;  // byte offset of this thread's first row
-    auto prefetch = [&](int chunk) {
+
+    auto prefetch_k = [&](int chunk) {
+        const int off = chunk * C * kD * 2 + ld_off;
+#pragma unroll
+        for (int p = 0; p < G::TPT; ++p)
+            raw_k[p] = bload16(rK, off + p * kD * 2);
+    };
+    auto prefetch_qv = [&](int chunk) {
         const int off = chunk * C * kD * 2 + ld_off;
 #pragma unroll
         for (int p = 0; p < G::TPT; ++p) {
             if (!SUMMARY)
                 raw_q[p] = bload16(rQ, off + p * kD * 2);
-            raw_k[p] = bload16(rK, off + p * kD * 2);
             raw_v[p] = bload16(rV, off + p * kD * 2);
         }
+    };
+    auto prefetch_a = [&](int chunk) {
         if (GATED && wave == 0) {
 #pragma unroll
             for (int h = 0; h < C / 64; ++h)
@@ -233,8 +273,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
         }
     };
 
+    // ---------------------------------------------------------------- gates
     // wave 0: inclusive scans of log(alpha) and of the last zero-gate position
-    auto gate_scan = [&](int n, int b) {
+    auto gate_scan = [&](int n, int gs) {
         if (GATED && wave == 0) {
             float carry = 0.f;
             int zcarry = -1;
@@ -255,249 +296,233 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                 }
                 s += carry;
                 zf = max(zf, zcarry);
-                sm.lg[b][j] = s;
-                sm.zp[b][j] = zf;
-                sm.gj[b][j] = zf >= 0 ? 0.f : __expf(s);
+                sm.lg[gs][j] = s;
+                sm.zp[gs][j] = zf;
+                sm.gj[gs][j] = zf >= 0 ? 0.f : __expf(s);
                 carry = __shfl(s, 63, 64);
                 zcarry = __shfl(zf, 63, 64);
             }
         }
     };
-
-    auto pair_decay = [&](int b, int j, int i) -> float {  // gates of tokens i+1..j
-        return sm.zp[b][j] > i ? 0.f : __expf(sm.lg[b][j] - sm.lg[b][i]);
+    auto pair_decay = [&](int gs, int j, int i) -> float {  // gates of tokens i+1..j
+        return sm.zp[gs][j] > i ? 0.f : __expf(sm.lg[gs][j] - sm.lg[gs][i]);
     };
 
-    auto stage = [&](int n, int b) {
-        // keys: phi, row-major K~ for the scores, gate-weighted token-major K~ for the
-        // state write, and the partial normaliser sums.  Tokens past the end of the
-        // segment load as zeros: their V rows are zero, so they add nothing to the
-        // state; they are masked in the scores by causality and here by w = 0.
-        {
-            float zacc[8];
+    // ---------------------------------------------------------------- staging
+    // keys: phi, row-major K~ for the scores, gate-weighted token-major K~ for the state
+    // write, and the partial normaliser sums.  Tokens past the end of the segment load as
+    // zeros: their V rows are zero, so they add nothing to the state; they are masked in
+    // the scores by causality and in the normaliser by w = 0.
+    auto stage_k = [&](int n, int gs, int buf) {
+        float zacc[8];
 #pragma unroll
-            for (int s = 0; s < 8; ++s)
-                zacc[s] = 0.f;
-            unsigned kwp[G::TPT][4];  // bf16 pairs of w*phi(k), feature pairs
+        for (int s = 0; s < 8; ++s)
+            zacc[s] = 0.f;
+        unsigned kwp[G::TPT][4];  // bf16 pairs of w*phi(k)
 #pragma unroll
-            for (int p = 0; p < G::TPT; ++p) {
-                const int j = tg * G::TPT + p;
-                const float w = j >= n ? 0.f : (GATED ? pair_decay(b, n - 1, j) : 1.f);
-                float x[8];
-                unpack8(raw_k[p], x);
-                bf16x8 kb;
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const float f = phi(x[s]);
-                    kb[s] = static_cast<bf16>(f);
-                    zacc[s] = fmaf(w, f, zacc[s]);
-                    if (GATED)
-                        x[s] = w * f;
-                }
-                if (!SUMMARY)
-                    *reinterpret_cast<bf16x8 *>(&sm.Ks[qk_off(j, fg * 8)]) = kb;
-                if (GATED) {
-                    bf16x8 kwb;
-#pragma unroll
-                    for (int s = 0; s < 8; ++s)
-                        kwb[s] = static_cast<bf16>(x[s]);
-                    const uint4 u = *reinterpret_cast<uint4 *>(&kwb);
-                    kwp[p][0] = u.x, kwp[p][1] = u.y, kwp[p][2] = u.z, kwp[p][3] = u.w;
-                } else {
-                    const uint4 u = *reinterpret_cast<uint4 *>(&kb);
-                    kwp[p][0] = u.x, kwp[p][1] = u.y, kwp[p][2] = u.z, kwp[p][3] = u.w;
-                }
-            }
+        for (int p = 0; p < G::TPT; ++p) {
+            const int j = tg * G::TPT + p;
+            const float w = j >= n ? 0.f : (GATED ? pair_decay(gs, n - 1, j) : 1.f);
+            float x[8];
+            unpack8(raw_k[p], x);
+            bf16x8 kb;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const int row = fg * 8 + s;
-                unsigned o[G::TPT / 2];
-#pragma unroll
-                for (int q = 0; q < G::TPT / 2; ++q)
-                    o[q] = (s & 1) ? pack_hi(kwp[2 * q][s >> 1], kwp[2 * q + 1][s >> 1])
-                                   : pack_lo(kwp[2 * q][s >> 1], kwp[2 * q + 1][s >> 1]);
-                if constexpr (G::TPT == 2)
-                    *reinterpret_cast<unsigned *>(&sm.KwT[tm_off<C>(row, tg * 2)]) = o[0];
-                else
-                    *reinterpret_cast<uint2 *>(&sm.KwT[tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
-                zacc[s] += __shfl_xor(zacc[s], 16, 64);
-                zacc[s] += __shfl_xor(zacc[s], 32, 64);
+                const float f = phi(x[s]);
+                kb[s] = static_cast<bf16>(f);
+                zacc[s] = fmaf(w, f, zacc[s]);
+                if (GATED)
+                    x[s] = w * f;
             }
-            if (lg4 == 0) {
+            if (!SUMMARY)
+                *reinterpret_cast<bf16x8 *>(&sm.Ks[buf][qk_off(j, fg * 8)]) = kb;
+            uint4 u;
+            if (GATED) {
+                bf16x8 kwb;
 #pragma unroll
                 for (int s = 0; s < 8; ++s)
-                    sm.zpart[wave * kD + fg * 8 + s] = zacc[s];
+                    kwb[s] = static_cast<bf16>(x[s]);
+                u = *reinterpret_cast<uint4 *>(&kwb);
+            } else {
+                u = *reinterpret_cast<uint4 *>(&kb);
             }
+            kwp[p][0] = u.x, kwp[p][1] = u.y, kwp[p][2] = u.z, kwp[p][3] = u.w;
         }
-        // queries: phi, row-major Q~ and the read of z_prev
-        if (!SUMMARY) {
 #pragma unroll
-            for (int p = 0; p < G::TPT; ++p) {
-                const int j = tg * G::TPT + p;
-                float x[8];
-                unpack8(raw_q[p], x);
-                bf16x8 qb;
-                float dot = 0.f;
+        for (int s = 0; s < 8; ++s) {
+            const int row = fg * 8 + s;
+            unsigned o[G::TPT / 2];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const float f = phi(x[s]);
-                    qb[s] = static_cast<bf16>(f);
-                    dot += f * sm.zs[fg * 8 + s];
-                }
-                *reinterpret_cast<bf16x8 *>(&sm.Qs[qk_off(j, fg * 8)]) = qb;
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1)
-                    dot += __shfl_xor(dot, off, 64);
-                if (fg == 0)
-                    sm.den_q[j] = dot;
-            }
+            for (int q = 0; q < G::TPT / 2; ++q)
+                o[q] = (s & 1) ? pack_hi(kwp[2 * q][s >> 1], kwp[2 * q + 1][s >> 1])
+                               : pack_lo(kwp[2 * q][s >> 1], kwp[2 * q + 1][s >> 1]);
+            if constexpr (G::TPT == 2)
+                *reinterpret_cast<unsigned *>(&sm.KwT[buf][tm_off<C>(row, tg * 2)]) = o[0];
+            else
+                *reinterpret_cast<uint2 *>(&sm.KwT[buf][tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
+            zacc[s] = xor32_sum(xor16_sum(zacc[s]));
         }
-        // values -> token-major VT: value column 8fg+s gets this thread's TPT tokens
-        {
-            unsigned w[G::TPT][4];
+        if (lg4 == 0) {
 #pragma unroll
-            for (int p = 0; p < G::TPT; ++p) {
-                w[p][0] = raw_v[p].x;
-                w[p][1] = raw_v[p].y;
-                w[p][2] = raw_v[p].z;
-                w[p][3] = raw_v[p].w;
-            }
+            for (int s = 0; s < 8; ++s)
+                sm.zpart[buf][wave * kD + fg * 8 + s] = zacc[s];
+        }
+    };
+    // queries: phi, row-major Q~ and the read of z_prev (z in sm.zs)
+    auto stage_q = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < G::TPT; ++p) {
+            const int j = tg * G::TPT + p;
+            float x[8];
+            unpack8(raw_q[p], x);
+            bf16x8 qb;
+            float dot = 0.f;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const int row = fg * 8 + s;
-                unsigned o[G::TPT / 2];
-#pragma unroll
-                for (int q = 0; q < G::TPT / 2; ++q)
-                    o[q] = (s & 1) ? pack_hi(w[2 * q][s >> 1], w[2 * q + 1][s >> 1])
-                                   : pack_lo(w[2 * q][s >> 1], w[2 * q + 1][s >> 1]);
-                if constexpr (G::TPT == 2)
-                    *reinterpret_cast<unsigned *>(&sm.VT[tm_off<C>(row, tg * 2)]) = o[0];
-                else
-                    *reinterpret_cast<uint2 *>(&sm.VT[tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
+                const float f = phi(x[s]);
+                qb[s] = static_cast<bf16>(f);
+                dot = fmaf(f, sm.zs[fg * 8 + s], dot);
             }
+            *reinterpret_cast<bf16x8 *>(&sm.Qs[buf][qk_off(j, fg * 8)]) = qb;
+            dot = row_sum16(dot);
+            if (fg == 0)
+                sm.den_q[buf][j] = dot;
+        }
+    };
+    // values -> token-major VT: value column 8fg+s gets this thread's TPT tokens
+    auto stage_v = [&](int buf) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int row = fg * 8 + s;
+            unsigned o[G::TPT / 2];
+#pragma unroll
+            for (int q = 0; q < G::TPT / 2; ++q) {
+                const unsigned lo = (&raw_v[2 * q].x)[s >> 1], hi = (&raw_v[2 * q + 1].x)[s >> 1];
+                o[q] = (s & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
+            }
+            if constexpr (G::TPT == 2)
+                *reinterpret_cast<unsigned *>(&sm.VT[buf][tm_off<C>(row, tg * 2)]) = o[0];
+            else
+                *reinterpret_cast<uint2 *>(&sm.VT[buf][tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
         }
     };
 
-    prefetch(0);
-    gate_scan((int)min((int64_t)C, len), 0);
-    __syncthreads();
-
-    for (int chunk = 0; chunk < n_chunks; ++chunk) {
-        const int64_t t0 = (int64_t)chunk * C;
-        const int n = (int)min((int64_t)C, len - t0);
-        const int b = chunk & 1;
-        const bool more = chunk + 1 < n_chunks;
-
-        stage(n, b);
-        if (more)
-            prefetch(chunk + 1);
-        __syncthreads();  // A: chunk staged
-
-        if (!SUMMARY) {
-            // ------------------------------------------------ (1) A tiles, distributed
-            for (int k = wave; k < G::NPT; k += 8) {
-                int tj = 0;
-                while ((tj + 1) * (tj + 2) / 2 <= k)
-                    ++tj;
-                const int ti = k - tj * (tj + 1) / 2;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // ---------------------------------------------------------------- chunk products
+    // (1) A tiles on or below the diagonal, distributed over the waves
+    auto scores = [&](int buf, int gs) {
+        for (int k = wave; k < G::NPT; k += 8) {
+            int tj = 0;
+            while ((tj + 1) * (tj + 2) / 2 <= k)
+                ++tj;
+            const int ti = k - tj * (tj + 1) / 2;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kf = 0; kf < 4; ++kf) {
-                    const bf16x8 ka =
-                        *reinterpret_cast<const bf16x8 *>(&sm.Ks[qk_off(ti * 16 + lr, kf * 32 + lg4 * 8)]);
-                    const bf16x8 qb =
-                        *reinterpret_cast<const bf16x8 *>(&sm.Qs[qk_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
-                    acc = mfma(ka, qb, acc);
-                }
-                // acc[r] = A[j][i], j = 16tj + lr, i = 16ti + 4lg4 + r
-                const int j = tj * 16 + lr;
-                float rsum = 0.f;
-                bf16x4 pk;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = ti * 16 + lg4 * 4 + r;
-                    float v = i <= j ? acc[r] : 0.f;
-                    if (GATED && i <= j)
-                        v *= pair_decay(b, j, i);
-                    rsum += v;
-                    pk[r] = static_cast<bf16>(v);
-                }
-                sm.P[k * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
-                rsum += __shfl_xor(rsum, 16, 64);
-                rsum += __shfl_xor(rsum, 32, 64);
-                if (lg4 == 0)
-                    sm.rs[k * 16 + lr] = rsum;
+            for (int kf = 0; kf < 4; ++kf) {
+                const bf16x8 ka =
+                    *reinterpret_cast<const bf16x8 *>(&sm.Ks[buf][qk_off(ti * 16 + lr, kf * 32 + lg4 * 8)]);
+                const bf16x8 qb =
+                    *reinterpret_cast<const bf16x8 *>(&sm.Qs[buf][qk_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
+                acc = mfma(ka, qb, acc);
             }
-            __syncthreads();  // B: A tiles and row sums ready
-
-            if (tid < C) {
-                const int tj = tid >> 4, jr = tid & 15;
-                float d = 0.f;
-                for (int ti = 0; ti <= tj; ++ti)
-                    d += sm.rs[(tj * (tj + 1) / 2 + ti) * 16 + jr];
-                const float inter = GATED ? sm.gj[b][tid] * sm.den_q[tid] : sm.den_q[tid];
-                sm.inv_den[tid] = 1.f / (inter + d + a.eps);
+            // acc[r] = A[j][i], j = 16tj + lr, i = 16ti + 4lg4 + r
+            const int j = tj * 16 + lr;
+            float rsum = 0.f;
+            bf16x4 pk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ti * 16 + lg4 * 4 + r;
+                float v = i <= j ? acc[r] : 0.f;
+                if (GATED && i <= j)
+                    v *= pair_decay(gs, j, i);
+                rsum += v;
+                pk[r] = static_cast<bf16>(v);
             }
-            __syncthreads();  // B': denominators ready
-
-            // ------------------------------------------------ (2) + (3) + output, my columns
-            // S_prev as the B operand: K step kf takes feature tiles 2kf and 2kf+1, whose
-            // accumulator rows 4lg4..4lg4+3 give the permuted k order used on both sides
-            bf16x8 sb[4];
+            sm.P[k * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
+            rsum = xor32_sum(xor16_sum(rsum));
+            if (lg4 == 0)
+                sm.rs[k * 16 + lr] = rsum;
+        }
+    };
+    // 1 / (denominator + eps) for chunk rows j0, j0 + step, ...
+    auto inv_den = [&](int buf, int gs, float *dst, int j0, int step) {
+        for (int j = j0; j < C; j += step) {
+            const int tj = j >> 4, jr = j & 15;
+            float d = 0.f;
+            for (int ti = 0; ti <= tj; ++ti)
+                d += sm.rs[(tj * (tj + 1) / 2 + ti) * 16 + jr];
+            const float inter = GATED ? sm.gj[gs][j] * sm.den_q[buf][j] : sm.den_q[buf][j];
+            dst[j] = 1.f / (inter + d + a.eps);
+        }
+    };
+    // (2) + (3) for this wave's 16 value columns, outputs through the dead K~ tile
+    auto outputs = [&](int buf, int gs, int64_t t0, const float *ivd) {
+        bf16 *ystage = sm.Ks[buf] + wave * (C * 16);
+        // S_prev as the B operand: K step kf takes feature tiles 2kf and 2kf+1, whose
+        // accumulator rows 4lg4..4lg4+3 give the permuted k order used on both sides
+        bf16x8 sb[4];
 #pragma unroll
-            for (int kf = 0; kf < 4; ++kf)
+        for (int kf = 0; kf < 4; ++kf)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    sb[kf][r] = static_cast<bf16>(sacc[2 * kf][r]);
-                    sb[kf][4 + r] = static_cast<bf16>(sacc[2 * kf + 1][r]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                sb[kf][r] = static_cast<bf16>(sacc[2 * kf][r]);
+                sb[kf][4 + r] = static_cast<bf16>(sacc[2 * kf + 1][r]);
+            }
 #pragma unroll 1
-            for (int tj = 0; tj < G::NTJ; ++tj) {
-                const int j = tj * 16 + lr;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int tj = 0; tj < G::NTJ; ++tj) {
+            const int j = tj * 16 + lr;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kf = 0; kf < 4; ++kf) {
-                    const bf16x4 lo =
-                        *reinterpret_cast<const bf16x4 *>(&sm.Qs[qk_off(j, kf * 32 + lg4 * 4)]);
-                    const bf16x4 hi =
-                        *reinterpret_cast<const bf16x4 *>(&sm.Qs[qk_off(j, kf * 32 + 16 + lg4 * 4)]);
-                    const bf16x8 qa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    acc = mfma(qa, sb[kf], acc);
-                }
-                if (GATED) {
+            for (int kf = 0; kf < 4; ++kf) {
+                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&sm.Qs[buf][qk_off(j, kf * 32 + lg4 * 4)]);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&sm.Qs[buf][qk_off(j, kf * 32 + 16 + lg4 * 4)]);
+                const bf16x8 qa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc = mfma(qa, sb[kf], acc);
+            }
+            if (GATED) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[r] *= sm.gj[b][tj * 16 + lg4 * 4 + r];
-                }
-                // (3) intra-chunk part, 32 keys per step
-                for (int ki = 0; 2 * ki <= tj; ++ki) {
-                    const int k1 = tj * (tj + 1) / 2 + 2 * ki;
-                    const uint2 p1 = sm.P[k1 * 64 + lane];
-                    const uint2 p2 = 2 * ki + 1 <= tj ? sm.P[(k1 + 1) * 64 + lane] : make_uint2(0u, 0u);
-                    const bf16x4 a1 = *reinterpret_cast<const bf16x4 *>(&p1);
-                    const bf16x4 a2 = *reinterpret_cast<const bf16x4 *>(&p2);
-                    const bf16x8 pa = {a1[0], a1[1], a1[2], a1[3], a2[0], a2[1], a2[2], a2[3]};
-                    const bf16x4 vlo = *reinterpret_cast<const bf16x4 *>(&sm.VT[tm_off<C>(cw, ki * 32 + lg4 * 4)]);
-                    const bf16x4 vhi =
-                        *reinterpret_cast<const bf16x4 *>(&sm.VT[tm_off<C>(cw, ki * 32 + 16 + lg4 * 4)]);
-                    const bf16x8 vb = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
-                    acc = mfma(pa, vb, acc);
-                }
-                // rows past the end of the segment fall outside rY and are dropped
+                for (int r = 0; r < 4; ++r)
+                    acc[r] *= sm.gj[gs][tj * 16 + lg4 * 4 + r];
+            }
+            for (int ki = 0; 2 * ki <= tj; ++ki) {
+                const int k1 = tj * (tj + 1) / 2 + 2 * ki;
+                const uint2 p1 = sm.P[k1 * 64 + lane];
+                const uint2 p2 = 2 * ki + 1 <= tj ? sm.P[(k1 + 1) * 64 + lane] : make_uint2(0u, 0u);
+                const bf16x4 a1 = *reinterpret_cast<const bf16x4 *>(&p1);
+                const bf16x4 a2 = *reinterpret_cast<const bf16x4 *>(&p2);
+                const bf16x8 pa = {a1[0], a1[1], a1[2], a1[3], a2[0], a2[1], a2[2], a2[3]};
+                const bf16x4 vlo = *reinterpret_cast<const bf16x4 *>(&sm.VT[buf][tm_off<C>(cw, ki * 32 + lg4 * 4)]);
+                const bf16x4 vhi =
+                    *reinterpret_cast<const bf16x4 *>(&sm.VT[buf][tm_off<C>(cw, ki * 32 + 16 + lg4 * 4)]);
+                const bf16x8 vb = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+                acc = mfma(pa, vb, acc);
+            }
+            // stage the 16 columns of this wave: row j, 16-byte granule (col >> 3)
+            // swapped on odd multiples of 8 rows to spread the rows over the banks
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int jj = tj * 16 + lg4 * 4 + r;
-                    const bf16 yv = static_cast<bf16>(acc[r] * sm.inv_den[jj]);
-                    __builtin_amdgcn_raw_buffer_store_b16(*reinterpret_cast<const short *>(&yv), rY,
-                                                          (int)((t0 + jj) * kD + cw) * 2, 0, 0);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int jj = tj * 16 + lg4 * 4 + r;
+                const int g = (lr >> 3) ^ ((jj >> 3) & 1);
+                ystage[jj * 16 + g * 8 + (lr & 7)] = static_cast<bf16>(acc[r] * ivd[jj]);
             }
         }
-
-        // ---------------------------------------------------- (4) state write, my columns
-        const float g_end = GATED ? sm.gj[b][n - 1] : 1.f;
+        // write this wave's C x 16 block as 16-byte row segments; rows past the end of
+        // the segment fall outside rY and are dropped
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int q = 0; q < C / 32; ++q) {
+            const int idx = q * 64 + lane;
+            const int jj = idx >> 1, g = idx & 1;
+            const uint4 v = *reinterpret_cast<const uint4 *>(&ystage[jj * 16 + ((g ^ ((jj >> 3) & 1)) * 8)]);
+            const int off = (int)((t0 + jj) * kD + wave * 16 + g * 8) * 2;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), rY, off, 0, 0);
+        }
+    };
+    // (4) S = g_end S + (w K~)^T V for this wave's columns
+    auto state_write = [&](int buf, float g_end) {
         if (GATED) {
-            g_seg *= g_end;
 #pragma unroll
             for (int tf = 0; tf < 8; ++tf)
 #pragma unroll
@@ -506,23 +531,64 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
         }
 #pragma unroll
         for (int ki = 0; ki < G::NKI; ++ki) {
-            const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(&sm.VT[tm_off<C>(cw, ki * 32 + lg4 * 8)]);
+            const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(&sm.VT[buf][tm_off<C>(cw, ki * 32 + lg4 * 8)]);
 #pragma unroll
             for (int tf = 0; tf < 8; ++tf) {
                 const bf16x8 ka =
-                    *reinterpret_cast<const bf16x8 *>(&sm.KwT[tm_off<C>(tf * 16 + lr, ki * 32 + lg4 * 8)]);
+                    *reinterpret_cast<const bf16x8 *>(&sm.KwT[buf][tm_off<C>(tf * 16 + lr, ki * 32 + lg4 * 8)]);
                 sacc[tf] = mfma(ka, vb, sacc[tf]);
             }
         }
+    };
+    // z = g_end z + sum of this chunk's w phi(k) (threads 0..127)
+    auto z_update = [&](int buf, float g_end) {
         if (tid < kD) {
             float zsum = 0.f;
 #pragma unroll
             for (int w8 = 0; w8 < 8; ++w8)
-                zsum += sm.zpart[w8 * kD + tid];
+                zsum += sm.zpart[buf][w8 * kD + tid];
             sm.zs[tid] = g_end * sm.zs[tid] + zsum;
         }
+    };
+
+    // ---------------------------------------------------------------- walk: stage, then multiply
+    prefetch_k(0);
+    prefetch_qv(0);
+    prefetch_a(0);
+    gate_scan(chunk_len(0), 0);
+    __syncthreads();
+
+    for (int c = 0; c < n_chunks; ++c) {
+        const int64_t t0 = (int64_t)c * C;
+        const int n = chunk_len(c);
+        const int gs = c & 1;
+        const bool more = c + 1 < n_chunks;
+
+        stage_k(n, gs, 0);
+        if (!SUMMARY)
+            stage_q(0);
+        stage_v(0);
+        if (more) {
+            prefetch_k(c + 1);
+            prefetch_qv(c + 1);
+            prefetch_a(c + 1);
+        }
+        __syncthreads();  // A: chunk staged
+
+        if (!SUMMARY) {
+            scores(0, gs);
+            __syncthreads();  // B: A tiles and row sums ready
+            inv_den(0, gs, sm.ivd, tid, kThreads);
+            __syncthreads();  // B': denominators ready
+            outputs(0, gs, t0, sm.ivd);
+        }
+        const float g_end = GATED ? sm.gj[gs][n - 1] : 1.f;
+        if (GATED)
+            g_seg *= g_end;
+        state_write(0, g_end);
+        z_update(0, g_end);
         if (more)
-            gate_scan((int)min((int64_t)C, len - t0 - C), b ^ 1);
+            gate_scan(chunk_len(c + 1), gs ^ 1);
         __syncthreads();  // C: chunk done
     }
 
@@ -585,7 +651,10 @@ hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)(n_heads * a.nseg);
     if (a.nseg > 1) {
-        chunk_kernel<C, GATED, true><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
+        // pass 1 walks 128-token chunks whatever the caller's chunk: its chunking only
+        // changes the rounding of the segment maps, and longer chunks keep more bytes
+        // in flight
+        chunk_kernel<128, GATED, true><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -626,7 +695,7 @@ hipError_t launch_prefill_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
     // work (two resident workgroups per unit at chunk 64, one at chunk 128), each
     // segment a whole number of chunks and long enough to hold its slot in Y.
     const int C = pa.chunk;
-    const int64_t target = C == 64 ? 512 : 256;
+    const int64_t target = C == 64 ? LA_SEGMENT_TARGET_C64 : LA_SEGMENT_TARGET_C128;
     int64_t nseg = (target + pa.n_heads - 1) / pa.n_heads;
     const int64_t min_len = ((kMinSegTokens + C - 1) / C) * C;
     if (nseg > pa.T / min_len)
