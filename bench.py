@@ -16,10 +16,13 @@ line also carries:
   cpu_baseline  the FP64 oracle timed on this host's cores on a sample of the
                 prefill workload.
 Run: python bench.py [--gpus 1] [--steps K] [--warmup W]
+     python bench.py --only prefill|decode|copy   (one workload, for profiler runs; `copy`
+     is a plain 1 GiB device-to-device copy used to calibrate the HBM byte counters)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +35,37 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 STATE_BYTES = 128 * 128 * 4 + 128 * 4
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+KERNEL_SOURCES = {
+    "prefill": ["prefill_mfma.hip", "kernels_general.hip"],
+    "decode": ["kernels_general.hip"],
+}
+
+
+def source_digest(kind):
+    """sha256 over the kernel sources of a path; counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "recurrent_state_chunkwise_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind):
+    """HBM bytes per call from the committed counter summary, if it matches these sources."""
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            for line in f:
+                line = line.strip()
+                if line.startswith("{"):
+                    rec = json.loads(line)
+                    if rec.get("kind") == kind and rec.get("source_sha256") == source_digest(kind):
+                        return rec["hbm_bytes_per_call"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def prefill_bytes(B, H, T, gated):
@@ -77,7 +111,7 @@ def time_prefill(torch, la, wl, cfg, steps, warmup):
     return total_ms, call_ms, wall
 
 
-def time_decode(torch, la, wl, cfg, warmup=10):
+def time_decode(torch, la, wl, cfg, warmup=10, steps=None):
     N = cfg.n_states
     # seed every state with 256 writes through the prefill path (untimed)
     ks, vs = wl.decode_seed_inputs(cfg, "cuda")
@@ -88,8 +122,8 @@ def time_decode(torch, la, wl, cfg, warmup=10):
     la.la_prefill_chunked(ks, ks, vs, None, cfg.eps, 64, Ys, S, z)
     del ks, vs, Ys
     S, z = S.view(N, cfg.d, cfg.dv), z.view(N, cfg.d)
-    steps = cfg.steps
-    inputs = [wl.decode_step_inputs(cfg, i, "cuda") for i in range(steps)]
+    steps = cfg.steps if steps is None else steps
+    inputs = [wl.decode_step_inputs(cfg, i, "cuda") for i in range(max(steps, warmup))]
     y = torch.empty((N, cfg.dv), device="cuda", dtype=torch.bfloat16)
     Sw, zw = S.clone(), z.clone()
     for i in range(warmup):  # on a scratch copy of the state
@@ -145,6 +179,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the decode and gated workloads")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run one workload only and print its timing (for profiler runs)")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="decode steps to time with --only decode (default: the workload's 1024)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -158,6 +196,20 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     la.library()
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}))
+        return
+    if args.only == "decode":
+        steps = args.decode_steps or wl.DECODE.steps
+        d_total, d_call = time_decode(torch, la, wl, wl.DECODE, steps=steps)
+        print(json.dumps({"only": "decode", "steps": steps, "ms_per_step": d_total / steps, "call_ms": d_call}))
+        return
     cfg = wl.PREFILL_UNGATED
     torch.cuda.synchronize()
     total_ms, call_ms, wall = time_prefill(torch, la, wl, cfg, args.steps, args.warmup)
@@ -190,13 +242,16 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("prefill"),
             "call_ms": call_ms,
             "algorithmic_bytes": nbytes,
             "useful_mfma_tflops": flops / (call_ms / 1e3) / 1e12,
             "mfma_frac": flops / (call_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
         },
     }
+    if args.only == "prefill":
+        print(json.dumps(out), flush=True)
+        return
     if not args.no_extra:
         dcfg = wl.DECODE
         d_total, d_call = time_decode(torch, la, wl, dcfg)
@@ -207,7 +262,8 @@ def main():
             "ms_per_step": d_total / dcfg.steps,
             "roofline": {"kernel": "la_decode_step", "bound": "hbm",
                          "achieved": d_bytes / (d_call / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": d_bytes / (d_call / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                         "frac": d_bytes / (d_call / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode"),
                          "call_ms": d_call, "algorithmic_bytes": d_bytes},
         }
         other = []
