@@ -326,6 +326,8 @@ hipError_t launch_general_typed(const PrefillArgs &a, hipStream_t stream)
 // d = dv = 128: one workgroup of 256 threads per state.  Thread (rg, cg) owns
 // VEC consecutive columns (cg) of the rows rg, rg + NRG, ..., so each wave reads
 // adjacent full rows; all of a thread's rows are loaded before any is used.
+// Each state is touched once per step, so its loads and stores are marked
+// non-temporal to keep it from displacing other lines in the caches.
 template <typename TI, typename TA, int VEC>
 __global__ __launch_bounds__(kThreads) void decode_w128_kernel(
     const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v, const TA *__restrict__ alpha,
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void decode_w128_kernel(
     vec_t s[ROWS];
 #pragma unroll
     for (int i = 0; i < ROWS; ++i)
-        s[i] = Sv[(rg + i * NRG) * NCG + cg];
+        s[i] = __builtin_nontemporal_load(&Sv[(rg + i * NRG) * NCG + cg]);
     const TA zf = tid < D ? z[n * D + tid] : TA(0);
     if (tid < D) {
         kf[tid] = phi_accurate(to_acc<TA>(k[n * D + tid]));
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void decode_w128_kernel(
             s[i][e] = a * s[i][e] + kv * vs[cg * VEC + e];
             part[e] += qv * s[i][e];
         }
-        Sv[f * NCG + cg] = s[i];
+        __builtin_nontemporal_store(s[i], &Sv[f * NCG + cg]);
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e)

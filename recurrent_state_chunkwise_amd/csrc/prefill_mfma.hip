@@ -27,13 +27,15 @@
 //
 // Inside a workgroup (8 waves, all 128 value columns) every product is
 // v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
-//   (1) A^T = K~ Q~^T, 16x16 tiles on or below the diagonal spread over the waves; the
-//       fp32 tile is masked and gate-weighted, its row sums feed the denominator and
-//       its accumulator layout is stored per lane as the A operand of (3);
-//   (2) N  = Q~ S_prev with S_prev taken from the fp32 state accumulators of the wave
-//   (3) N += A V
-//   (4) S  = g_last S + (w K~)^T V
-// Wave w owns value columns 16w..16w+15 of N and of S, so S never leaves registers.
+//   (1) scores K~ Q~^T, 16x16 tiles on or below the diagonal spread over the waves; the
+//       fp32 tile is masked, gate-weighted and kept in LDS as bf16 in accumulator layout;
+//   (2) N^T  = S_prev^T Q~^T  and  D = z_prev^T Q~^T, both scaled by exp(L_j);
+//   (3) N^T += V^T P^T        and  D += 1^T P^T (the row sums of the masked scores);
+//   (4) S = g_last S + (w K~)^T V  and  z = g_last z + (w K~)^T 1.
+// Wave w owns value columns 16w..16w+15 of N and of S and features 16w..16w+15 of z,
+// so S and z never leave registers; z goes through LDS once per chunk for (2).  The
+// outputs are computed transposed so that a lane holds four adjacent columns of one
+// token together with that token's denominator.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -118,41 +120,16 @@ struct alignas(16) Smem {
     typedef Cfg<C> G;
     static constexpr int QN = SUMMARY ? 1 : C * kD;
     static constexpr int PN = SUMMARY ? 1 : G::NPT;
-    alignas(16) bf16 Qs[1][QN];             // phi(q) rows
-    alignas(16) bf16 Ks[1][QN];             // phi(k) rows; after the scores, output staging
-    alignas(16) bf16 KwT[1][kD * C];
-    alignas(16) bf16 VT[1][kD * C];
-    alignas(16) uint2 P[PN * 64];           // bf16 A tiles, one 4-value group per lane
-    alignas(16) float rs[PN * 16];          // row sums of each A tile
-    alignas(16) float zpart[1][8 * kD];     // per-wave partial sums of w phi(k)
-    alignas(16) float zs[kD];
-    alignas(16) float den_q[1][C];          // phi(q_j) . z_prev
-    alignas(16) float ivd[C];               // 1 / (denominator + eps)
-    alignas(16) float lg[2][C];             // in-chunk prefix sum of log(alpha) (0 at zero gates)
-    alignas(16) float gj[2][C];             // product of the chunk's gates up to j
-    alignas(16) int zp[2][C];               // last zero gate at or before j, -1 if none
+    alignas(16) bf16 Qs[QN];         // phi(q) rows
+    alignas(16) bf16 Ks[QN];         // phi(k) rows
+    alignas(16) bf16 KwT[kD * C];    // w phi(k), token-major
+    alignas(16) bf16 VT[kD * C];     // values, token-major
+    alignas(16) uint2 P[PN * 64];    // bf16 score tiles, one 4-value group per lane
+    alignas(16) float zs[2][kD];     // z entering the chunk, by chunk parity
+    alignas(16) float lg[2][C];      // in-chunk prefix sum of log(alpha) (0 at zero gates)
+    alignas(16) float gj[2][C];      // product of the chunk's gates up to j
+    alignas(16) int zp[2][C];        // last zero gate at or before j, -1 if none
 };
-
-// Sum over the 16 lanes of a DPP row, result in every lane of the row.
-__device__ __forceinline__ float row_sum16(float v)
-{
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));  // row_ror:4
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false));  // row_ror:2
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false));  // row_ror:1
-    return v;
-}
-// v[l] + v[l ^ 16] and v[l] + v[l ^ 32] with the gfx950 lane-swap instructions
-__device__ __forceinline__ float xor16_sum(float v)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float v)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // swizzled element offsets
 __device__ __forceinline__ int qk_off(int row, int col)  // [C][128]
@@ -218,16 +195,23 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
     const rsrc_t rY = make_rsrc(a.Y + row0 * kD, len * kD * 2);
     const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
 
+    bf16x8 ones;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        ones[s] = static_cast<bf16>(1.f);
+
     // ---------------------------------------------------------------- entering state
-    // wave w owns value columns c = 16w + lr; tile tf holds rows f = 16tf + 4lg4 + r
+    // wave w owns value columns c = 16w + lr of S (tile tf holds rows f = 16tf + 4lg4 + r)
+    // and features f = 16w + 4lg4 + r of z
     f32x4 sacc[8];
+    f32x4 zr;
     const int cw = wave * 16 + lr;
+    const int fw = wave * 16 + lg4 * 4;
     if (SUMMARY) {
 #pragma unroll
         for (int tf = 0; tf < 8; ++tf)
             sacc[tf] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tid < kD)
-            sm.zs[tid] = 0.f;
+        zr = f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
         const float *Sin = a.nseg == 1 ? a.S + head * kD * kD : slot_ptr(a, head, seg);
         const float *zin = a.nseg == 1 ? a.z + head * kD : Sin + kD * kD;
@@ -236,8 +220,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 sacc[tf][r] = Sin[(tf * 16 + lg4 * 4 + r) * kD + cw];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zr[r] = zin[fw + r];
         if (tid < kD)
-            sm.zs[tid] = zin[tid];
+            sm.zs[0][tid] = zin[tid];
     }
     float g_seg = 1.f;  // product of all gates of the segment (SUMMARY)
 
@@ -309,15 +296,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
     };
 
     // ---------------------------------------------------------------- staging
-    // keys: phi, row-major K~ for the scores, gate-weighted token-major K~ for the state
-    // write, and the partial normaliser sums.  Tokens past the end of the segment load as
-    // zeros: their V rows are zero, so they add nothing to the state; they are masked in
-    // the scores by causality and in the normaliser by w = 0.
-    auto stage_k = [&](int n, int gs, int buf) {
-        float zacc[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            zacc[s] = 0.f;
+    // keys: phi, row-major K~ for the scores and the token-major write weights
+    // w_j phi(k_j) (w_j = gates after j to the chunk end, 0 past the end of the segment,
+    // whose tokens load as zeros); values: token-major V.
+    auto stage_k = [&](int n, int gs) {
         unsigned kwp[G::TPT][4];  // bf16 pairs of w*phi(k)
 #pragma unroll
         for (int p = 0; p < G::TPT; ++p) {
@@ -330,12 +312,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
             for (int s = 0; s < 8; ++s) {
                 const float f = phi(x[s]);
                 kb[s] = static_cast<bf16>(f);
-                zacc[s] = fmaf(w, f, zacc[s]);
                 if (GATED)
                     x[s] = w * f;
             }
             if (!SUMMARY)
-                *reinterpret_cast<bf16x8 *>(&sm.Ks[buf][qk_off(j, fg * 8)]) = kb;
+                *reinterpret_cast<bf16x8 *>(&sm.Ks[qk_off(j, fg * 8)]) = kb;
             uint4 u;
             if (GATED) {
                 bf16x8 kwb;
@@ -344,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                     kwb[s] = static_cast<bf16>(x[s]);
                 u = *reinterpret_cast<uint4 *>(&kwb);
             } else {
-                u = *reinterpret_cast<uint4 *>(&kb);
+                u = j < n ? *reinterpret_cast<uint4 *>(&kb) : make_uint4(0u, 0u, 0u, 0u);
             }
             kwp[p][0] = u.x, kwp[p][1] = u.y, kwp[p][2] = u.z, kwp[p][3] = u.w;
         }
@@ -357,40 +338,26 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                 o[q] = (s & 1) ? pack_hi(kwp[2 * q][s >> 1], kwp[2 * q + 1][s >> 1])
                                : pack_lo(kwp[2 * q][s >> 1], kwp[2 * q + 1][s >> 1]);
             if constexpr (G::TPT == 2)
-                *reinterpret_cast<unsigned *>(&sm.KwT[buf][tm_off<C>(row, tg * 2)]) = o[0];
+                *reinterpret_cast<unsigned *>(&sm.KwT[tm_off<C>(row, tg * 2)]) = o[0];
             else
-                *reinterpret_cast<uint2 *>(&sm.KwT[buf][tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
-            zacc[s] = xor32_sum(xor16_sum(zacc[s]));
-        }
-        if (lg4 == 0) {
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                sm.zpart[buf][wave * kD + fg * 8 + s] = zacc[s];
+                *reinterpret_cast<uint2 *>(&sm.KwT[tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
         }
     };
-    // queries: phi, row-major Q~ and the read of z_prev (z in sm.zs)
-    auto stage_q = [&](int buf) {
+    auto stage_q = [&]() {
 #pragma unroll
         for (int p = 0; p < G::TPT; ++p) {
             const int j = tg * G::TPT + p;
             float x[8];
             unpack8(raw_q[p], x);
             bf16x8 qb;
-            float dot = 0.f;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const float f = phi(x[s]);
-                qb[s] = static_cast<bf16>(f);
-                dot = fmaf(f, sm.zs[fg * 8 + s], dot);
-            }
-            *reinterpret_cast<bf16x8 *>(&sm.Qs[buf][qk_off(j, fg * 8)]) = qb;
-            dot = row_sum16(dot);
-            if (fg == 0)
-                sm.den_q[buf][j] = dot;
+            for (int s = 0; s < 8; ++s)
+                qb[s] = static_cast<bf16>(phi(x[s]));
+            *reinterpret_cast<bf16x8 *>(&sm.Qs[qk_off(j, fg * 8)]) = qb;
         }
     };
-    // values -> token-major VT: value column 8fg+s gets this thread's TPT tokens
-    auto stage_v = [&](int buf) {
+    // value column 8fg+s gets this thread's TPT tokens
+    auto stage_v = [&]() {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int row = fg * 8 + s;
@@ -401,15 +368,17 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                 o[q] = (s & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
             }
             if constexpr (G::TPT == 2)
-                *reinterpret_cast<unsigned *>(&sm.VT[buf][tm_off<C>(row, tg * 2)]) = o[0];
+                *reinterpret_cast<unsigned *>(&sm.VT[tm_off<C>(row, tg * 2)]) = o[0];
             else
-                *reinterpret_cast<uint2 *>(&sm.VT[buf][tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
+                *reinterpret_cast<uint2 *>(&sm.VT[tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
         }
     };
 
     // ---------------------------------------------------------------- chunk products
-    // (1) A tiles on or below the diagonal, distributed over the waves
-    auto scores = [&](int buf, int gs) {
+    // (1) score tiles on or below the diagonal, distributed over the waves.  The tile
+    // is K~ Q~^T, so lane (lr, lg4) holds scores (j = 16tj + lr, i = 16ti + 4lg4 + r),
+    // masked to i <= j and weighted by the gates of tokens i+1..j.
+    auto scores = [&](int gs) {
         for (int k = wave; k < G::NPT; k += 8) {
             int tj = 0;
             while ((tj + 1) * (tj + 2) / 2 <= k)
@@ -418,15 +387,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kf = 0; kf < 4; ++kf) {
-                const bf16x8 ka =
-                    *reinterpret_cast<const bf16x8 *>(&sm.Ks[buf][qk_off(ti * 16 + lr, kf * 32 + lg4 * 8)]);
-                const bf16x8 qb =
-                    *reinterpret_cast<const bf16x8 *>(&sm.Qs[buf][qk_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&sm.Ks[qk_off(ti * 16 + lr, kf * 32 + lg4 * 8)]);
+                const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&sm.Qs[qk_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
                 acc = mfma(ka, qb, acc);
             }
-            // acc[r] = A[j][i], j = 16tj + lr, i = 16ti + 4lg4 + r
             const int j = tj * 16 + lr;
-            float rsum = 0.f;
             bf16x4 pk;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -434,54 +399,52 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                 float v = i <= j ? acc[r] : 0.f;
                 if (GATED && i <= j)
                     v *= pair_decay(gs, j, i);
-                rsum += v;
                 pk[r] = static_cast<bf16>(v);
             }
             sm.P[k * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
-            rsum = xor32_sum(xor16_sum(rsum));
-            if (lg4 == 0)
-                sm.rs[k * 16 + lr] = rsum;
         }
     };
-    // 1 / (denominator + eps) for chunk rows j0, j0 + step, ...
-    auto inv_den = [&](int buf, int gs, float *dst, int j0, int step) {
-        for (int j = j0; j < C; j += step) {
-            const int tj = j >> 4, jr = j & 15;
-            float d = 0.f;
-            for (int ti = 0; ti <= tj; ++ti)
-                d += sm.rs[(tj * (tj + 1) / 2 + ti) * 16 + jr];
-            const float inter = GATED ? sm.gj[gs][j] * sm.den_q[buf][j] : sm.den_q[buf][j];
-            dst[j] = 1.f / (inter + d + a.eps);
-        }
-    };
-    // (2) + (3) for this wave's 16 value columns, outputs through the dead K~ tile
-    auto outputs = [&](int buf, int gs, int64_t t0, const float *ivd) {
-        bf16 *ystage = sm.Ks[buf] + wave * (C * 16);
-        // S_prev as the B operand: K step kf takes feature tiles 2kf and 2kf+1, whose
-        // accumulator rows 4lg4..4lg4+3 give the permuted k order used on both sides
-        bf16x8 sb[4];
+    // (2) + (3) for this wave's 16 value columns, computed transposed:
+    //   N^T = S_prev^T Q~^T (gated by g_j) + V^T P^T,   D = z_prev^T Q~^T (gated) + 1^T P^T
+    // Accumulator lane (lr, lg4) holds token j = 16tj + lr, columns fw .. fw + 3, and the
+    // denominator of token j, so each lane writes 8 contiguous bytes of y.  Operands of
+    // one K step are two 16-row tiles: rows 4lg4..4lg4+3 of each give the permuted k
+    // order, used alike on both sides of every product.
+    auto outputs = [&](int gs, int64_t t0, int zbuf) {
+        bf16x8 sb[4], zb[4];
 #pragma unroll
-        for (int kf = 0; kf < 4; ++kf)
+        for (int kf = 0; kf < 4; ++kf) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 sb[kf][r] = static_cast<bf16>(sacc[2 * kf][r]);
                 sb[kf][4 + r] = static_cast<bf16>(sacc[2 * kf + 1][r]);
             }
+            const f32x4 zlo = *reinterpret_cast<const f32x4 *>(&sm.zs[zbuf][kf * 32 + lg4 * 4]);
+            const f32x4 zhi = *reinterpret_cast<const f32x4 *>(&sm.zs[zbuf][kf * 32 + 16 + lg4 * 4]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                zb[kf][r] = static_cast<bf16>(zlo[r]);
+                zb[kf][4 + r] = static_cast<bf16>(zhi[r]);
+            }
+        }
 #pragma unroll 1
         for (int tj = 0; tj < G::NTJ; ++tj) {
             const int j = tj * 16 + lr;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, dac = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kf = 0; kf < 4; ++kf) {
-                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&sm.Qs[buf][qk_off(j, kf * 32 + lg4 * 4)]);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&sm.Qs[buf][qk_off(j, kf * 32 + 16 + lg4 * 4)]);
-                const bf16x8 qa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                acc = mfma(qa, sb[kf], acc);
+                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&sm.Qs[qk_off(j, kf * 32 + lg4 * 4)]);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&sm.Qs[qk_off(j, kf * 32 + 16 + lg4 * 4)]);
+                const bf16x8 qb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc = mfma(sb[kf], qb, acc);
+                dac = mfma(zb[kf], qb, dac);
             }
             if (GATED) {
+                const float g = sm.gj[gs][j];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[r] *= sm.gj[gs][tj * 16 + lg4 * 4 + r];
+                    acc[r] *= g;
+                dac[0] *= g;  // only element 0 of the denominator is read
             }
             for (int ki = 0; 2 * ki <= tj; ++ki) {
                 const int k1 = tj * (tj + 1) / 2 + 2 * ki;
@@ -489,66 +452,50 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                 const uint2 p2 = 2 * ki + 1 <= tj ? sm.P[(k1 + 1) * 64 + lane] : make_uint2(0u, 0u);
                 const bf16x4 a1 = *reinterpret_cast<const bf16x4 *>(&p1);
                 const bf16x4 a2 = *reinterpret_cast<const bf16x4 *>(&p2);
-                const bf16x8 pa = {a1[0], a1[1], a1[2], a1[3], a2[0], a2[1], a2[2], a2[3]};
-                const bf16x4 vlo = *reinterpret_cast<const bf16x4 *>(&sm.VT[buf][tm_off<C>(cw, ki * 32 + lg4 * 4)]);
-                const bf16x4 vhi =
-                    *reinterpret_cast<const bf16x4 *>(&sm.VT[buf][tm_off<C>(cw, ki * 32 + 16 + lg4 * 4)]);
-                const bf16x8 vb = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
-                acc = mfma(pa, vb, acc);
+                const bf16x8 pb = {a1[0], a1[1], a1[2], a1[3], a2[0], a2[1], a2[2], a2[3]};
+                const bf16x4 vlo = *reinterpret_cast<const bf16x4 *>(&sm.VT[tm_off<C>(cw, ki * 32 + lg4 * 4)]);
+                const bf16x4 vhi = *reinterpret_cast<const bf16x4 *>(&sm.VT[tm_off<C>(cw, ki * 32 + 16 + lg4 * 4)]);
+                const bf16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+                acc = mfma(va, pb, acc);
+                dac = mfma(ones, pb, dac);
             }
-            // stage the 16 columns of this wave: row j, 16-byte granule (col >> 3)
-            // swapped on odd multiples of 8 rows to spread the rows over the banks
+            const float inv = __builtin_amdgcn_rcpf(dac[0] + a.eps);
+            bf16x4 yb;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int jj = tj * 16 + lg4 * 4 + r;
-                const int g = (lr >> 3) ^ ((jj >> 3) & 1);
-                ystage[jj * 16 + g * 8 + (lr & 7)] = static_cast<bf16>(acc[r] * ivd[jj]);
-            }
-        }
-        // write this wave's C x 16 block as 16-byte row segments; rows past the end of
-        // the segment fall outside rY and are dropped
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int q = 0; q < C / 32; ++q) {
-            const int idx = q * 64 + lane;
-            const int jj = idx >> 1, g = idx & 1;
-            const uint4 v = *reinterpret_cast<const uint4 *>(&ystage[jj * 16 + ((g ^ ((jj >> 3) & 1)) * 8)]);
-            const int off = (int)((t0 + jj) * kD + wave * 16 + g * 8) * 2;
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), rY, off, 0, 0);
+            for (int r = 0; r < 4; ++r)
+                yb[r] = static_cast<bf16>(acc[r] * inv);
+            // rows past the end of the segment fall outside rY and are dropped
+            const int off = (int)((t0 + j) * kD + fw) * 2;
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, yb),
+                                                  rY, off, 0, 0);
         }
     };
-    // (4) S = g_end S + (w K~)^T V for this wave's columns
-    auto state_write = [&](int buf, float g_end) {
+    // (4) S = g_end S + (w K~)^T V for this wave's columns, and
+    //     z = g_end z + (w K~)^T 1 for this wave's features (published for the next chunk)
+    auto state_write = [&](float g_end, int znext) {
         if (GATED) {
 #pragma unroll
             for (int tf = 0; tf < 8; ++tf)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sacc[tf][r] *= g_end;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                zr[r] *= g_end;
         }
 #pragma unroll
         for (int ki = 0; ki < G::NKI; ++ki) {
-            const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(&sm.VT[buf][tm_off<C>(cw, ki * 32 + lg4 * 8)]);
+            const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(&sm.VT[tm_off<C>(cw, ki * 32 + lg4 * 8)]);
 #pragma unroll
             for (int tf = 0; tf < 8; ++tf) {
-                const bf16x8 ka =
-                    *reinterpret_cast<const bf16x8 *>(&sm.KwT[buf][tm_off<C>(tf * 16 + lr, ki * 32 + lg4 * 8)]);
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&sm.KwT[tm_off<C>(tf * 16 + lr, ki * 32 + lg4 * 8)]);
                 sacc[tf] = mfma(ka, vb, sacc[tf]);
             }
+            const bf16x8 kz = *reinterpret_cast<const bf16x8 *>(&sm.KwT[tm_off<C>(wave * 16 + lr, ki * 32 + lg4 * 8)]);
+            zr = mfma(kz, ones, zr);
         }
-    };
-    // z = g_end z + sum of this chunk's w phi(k) (threads 0..127)
-    auto z_update = [&](int buf, float g_end) {
-        if (tid < kD) {
-            float zsum = 0.f;
-#pragma unroll
-            for (int w8 = 0; w8 < 8; ++w8)
-                zsum += sm.zpart[buf][w8 * kD + tid];
-            sm.zs[tid] = g_end * sm.zs[tid] + zsum;
-        }
+        if (!SUMMARY && lr == 0)
+            *reinterpret_cast<f32x4 *>(&sm.zs[znext][fw]) = zr;
     };
 
     // ---------------------------------------------------------------- walk: stage, then multiply
@@ -564,10 +511,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
         const int gs = c & 1;
         const bool more = c + 1 < n_chunks;
 
-        stage_k(n, gs, 0);
+        stage_k(n, gs);
         if (!SUMMARY)
-            stage_q(0);
-        stage_v(0);
+            stage_q();
+        stage_v();
         if (more) {
             prefetch_k(c + 1);
             prefetch_qv(c + 1);
@@ -576,17 +523,14 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
         __syncthreads();  // A: chunk staged
 
         if (!SUMMARY) {
-            scores(0, gs);
-            __syncthreads();  // B: A tiles and row sums ready
-            inv_den(0, gs, sm.ivd, tid, kThreads);
-            __syncthreads();  // B': denominators ready
-            outputs(0, gs, t0, sm.ivd);
+            scores(gs);
+            __syncthreads();  // B: score tiles ready
+            outputs(gs, t0, c & 1);
         }
         const float g_end = GATED ? sm.gj[gs][n - 1] : 1.f;
         if (GATED)
             g_seg *= g_end;
-        state_write(0, g_end);
-        z_update(0, g_end);
+        state_write(g_end, (c + 1) & 1);
         if (more)
             gate_scan(chunk_len(c + 1), gs ^ 1);
         __syncthreads();  // C: chunk done
@@ -610,8 +554,458 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             Sout[(tf * 16 + lg4 * 4 + r) * kD + cw] = sacc[tf][r];
-    if (tid < kD)
-        zout[tid] = sm.zs[tid];
+    if (lr == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zout[fw + r] = zr[r];
+    }
+}
+
+// ============================================================================ pass 3, chunk 64
+// Producer / consumer form of the full pass at chunk 64: 12 waves, of which waves 0-7
+// (consumers) hold S and z and do every product, while waves 8-11 (producers) turn the
+// raw Q, K, V and alpha of the next chunk into staged tiles in the other half of a
+// double-buffered LDS.  Two workgroup barriers per chunk i:
+//   part a   consumers: scores of chunk i; N^T = S_prev^T Q~^T; waves 4-7 D = z_prev^T Q~^T
+//            producers: y of chunk i-1 to HBM; gate scan of chunk i+1; phi(q) and V of chunk i+1
+//   part b   consumers: gates, V^T P^T and 1^T P^T, y into LDS, state and z update
+//            producers: phi(k) and the write weights of chunk i+1
+// Each raw load is issued two chunks ahead of its use.  The two roles run their own
+// loops with the same number of barriers, which keeps their registers apart.
+//
+// Every staged tile is token-major (one row of 128 bf16 per token, rows padded to
+// 272 bytes), written with 16-byte row stores.  Operands that contract over tokens (V^T
+// for (3), the write weights and V for (4)) are read with the gfx950 transposing LDS
+// load: within each 16-lane group, lane 4e + q supplies the address of 4 adjacent
+// columns of token row t(e) and lane i receives column i of rows t(0..3).  With the
+// padded rows every row store, row read and transposing read of a wave hits distinct
+// banks as long as each transposing load takes only even or only odd token rows per
+// 32 lanes; the scores therefore feed K~ rows to the MFMA in the order sigma (even
+// tokens first), which makes the score tiles, and so V^T in (3), come in that order.
+constexpr int kPcC = 64;
+constexpr int kPcConsumers = 512;
+constexpr int kPcThreads = 768;
+
+constexpr int kRow = kD + 8;  // padded token row, in elements
+__device__ __forceinline__ int pr_off(int row, int col) { return row * kRow + col; }
+// token order of the K~ rows in the score tiles: even tokens of the 16-token tile first
+__device__ __forceinline__ int sigma(int m) { return 2 * (m & 7) + (m >> 3); }
+// y tile: 16-byte granule g of row j sits at granule g ^ (j & 15)
+__device__ __forceinline__ int ys_off(int row, int col)
+{
+    return row * kD + ((((col >> 3) ^ (row & 15)) << 3) | (col & 7));
+}
+// 4 bf16 of one lane from the transposing LDS load
+__device__ __forceinline__ bf16x4 ld_tr(const bf16 *p)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi)
+{
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <bool GATED>
+struct alignas(16) PcSmem {
+    alignas(16) bf16 Qs[2][kPcC * kRow];           // phi(q)
+    alignas(16) bf16 Ks[2][kPcC * kRow];           // phi(k); ungated, also the write weights
+    alignas(16) bf16 Vs[2][kPcC * kRow];           // v
+    alignas(16) bf16 Kw[GATED ? 2 : 1][GATED ? kPcC * kRow : 8];  // w phi(k) (gated)
+    alignas(16) bf16 Ys[kPcC * kD];                // y of the last finished chunk, granules XOR-swizzled by row
+    alignas(16) uint2 P[Cfg<kPcC>::NPT * 64];      // bf16 score tiles, one 4-value group per lane
+    alignas(16) float zs[2][kD];                   // z entering the chunk, by chunk parity
+    alignas(16) float dq[kPcC];                    // phi(q_j) . z_prev
+    alignas(16) float lg[2][kPcC];
+    alignas(16) float gj[2][kPcC];
+    alignas(16) int zp[2][kPcC];
+};
+
+// workgroup barrier with LDS visibility; reached the same number of times by every
+// wave, from the producer and the consumer loops alike
+__device__ __forceinline__ void wg_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <bool GATED>
+__global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
+{
+    constexpr int C = kPcC;
+    typedef Cfg<C> G;
+    __shared__ PcSmem<GATED> sm;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int lr = lane & 15;
+    const int lg4 = lane >> 4;
+
+    const int64_t head = blockIdx.x / a.nseg;
+    const int seg = blockIdx.x % a.nseg;
+    const int64_t s0 = (int64_t)seg * a.seg_len;
+    const int64_t s1 = seg == a.nseg - 1 ? a.T : s0 + a.seg_len;
+    const int64_t len = s1 - s0;
+    const int n_chunks = (int)((len + C - 1) / C);
+    auto chunk_len = [&](int c) { return (int)min((int64_t)C, len - (int64_t)c * C); };
+    const int64_t row0 = head * a.T + s0;
+
+    auto pair_decay = [&](int gs, int j, int i) -> float {  // gates of tokens i+1..j
+        return sm.zp[gs][j] > i ? 0.f : __expf(sm.lg[gs][j] - sm.lg[gs][i]);
+    };
+
+    if (wave >= 8) {
+        // ============================================================ producers
+        const rsrc_t rQ = make_rsrc(a.Q + row0 * kD, len * kD * 2);
+        const rsrc_t rK = make_rsrc(a.K + row0 * kD, len * kD * 2);
+        const rsrc_t rV = make_rsrc(a.V + row0 * kD, len * kD * 2);
+        const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
+        const rsrc_t rY = make_rsrc(a.Y + row0 * kD, len * kD * 2);
+        const int pt = tid - kPcConsumers;
+        const bool scanner = wave == 8;
+        // thread (fg, tg) stages granule fg (8 features) of tokens 4tg .. 4tg + 3
+        const int fg = pt & 15, tg = pt >> 4;
+        const int ld_off = tg * 4 * kD * 2 + fg * 16;
+        // two register sets: chunk c is loaded into set c & 1 two chunks before it is staged
+        uint4 rq0[4], rk0[4], rv0[4], rq1[4], rk1[4], rv1[4];
+        float ar0 = 0.f, ar1 = 0.f;
+
+        auto load_qv = [&](int c, uint4 (&rq)[4], uint4 (&rv)[4]) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                rq[p] = bload16(rQ, c * C * kD * 2 + ld_off + p * kD * 2);
+                rv[p] = bload16(rV, c * C * kD * 2 + ld_off + p * kD * 2);
+            }
+        };
+        auto load_k = [&](int c, uint4 (&rk)[4]) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                rk[p] = bload16(rK, c * C * kD * 2 + ld_off + p * kD * 2);
+        };
+        auto load_a = [&](int c, float &ar) {
+            if (GATED && scanner)
+                ar = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (c * C + lane) * 4, 0, 0));
+        };
+        // inclusive scans of log(alpha) and of the last zero-gate position (one wave)
+        auto scan = [&](int n, int gs, float ar) {
+            if (GATED && scanner) {
+                const float av = lane < n ? ar : 1.f;
+                float s = av > 0.f ? __logf(av) : 0.f;
+                int zf = av == 0.f ? lane : -1;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float s2 = __shfl_up(s, off, 64);
+                    const int z2 = __shfl_up(zf, off, 64);
+                    if (lane >= off) {
+                        s += s2;
+                        zf = max(zf, z2);
+                    }
+                }
+                sm.lg[gs][lane] = s;
+                sm.zp[gs][lane] = zf;
+                sm.gj[gs][lane] = zf >= 0 ? 0.f : __expf(s);
+            }
+        };
+        // phi(q) rows and V rows
+        auto stage_qv = [&](int buf, const uint4 (&rq)[4], const uint4 (&rv)[4]) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int j = tg * 4 + p;
+                float x[8];
+                unpack8(rq[p], x);
+                bf16x8 qb;
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    qb[s] = static_cast<bf16>(phi(x[s]));
+                *reinterpret_cast<bf16x8 *>(&sm.Qs[buf][pr_off(j, fg * 8)]) = qb;
+                *reinterpret_cast<uint4 *>(&sm.Vs[buf][pr_off(j, fg * 8)]) = rv[p];
+            }
+        };
+        // phi(k) rows and the write weights w_j phi(k_j); w_j = gates after j to the
+        // chunk end, 0 past the end of the segment (whose tokens load as zeros).  The
+        // ungated weights are phi(k) itself, so those rows of Ks are zeroed instead (the
+        // scores never use them: they lie above the diagonal of every kept row).
+        auto stage_k = [&](int buf, int gs, int n, const uint4 (&rk)[4]) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int j = tg * 4 + p;
+                float x[8];
+                unpack8(rk[p], x);
+                bf16x8 kb, kwb;
+                const float w = j >= n ? 0.f : (GATED ? pair_decay(gs, n - 1, j) : 1.f);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float f = phi(x[s]);
+                    kb[s] = static_cast<bf16>(f);
+                    if (GATED)
+                        kwb[s] = static_cast<bf16>(w * f);
+                }
+                uint4 u = *reinterpret_cast<uint4 *>(&kb);
+                if (!GATED && j >= n)
+                    u = make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4 *>(&sm.Ks[buf][pr_off(j, fg * 8)]) = u;
+                if (GATED)
+                    *reinterpret_cast<bf16x8 *>(&sm.Kw[buf][pr_off(j, fg * 8)]) = kwb;
+            }
+        };
+        // y of chunk c from the LDS tile to HBM as whole 256-byte rows: wave 8 + u takes
+        // rows 16u .. 16u + 15, four rows per store; rows past the end of the segment fall
+        // outside rY and are dropped
+        const int pw = wave - 8;
+        auto flush_y = [&](int c) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int row = pw * 16 + u * 4 + (lane >> 4), g = lane & 15;
+                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.Ys[row * kD + g * 8]);
+                const int off = ((c * C + row) * kD + ((g ^ (row & 15)) << 3)) * 2;
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), rY, off, 0, 0);
+            }
+        };
+        // one chunk interval: write out y of chunk i - 1, stage chunk cn = i + 1 from its
+        // register set, then refill that set with chunk cn + 2
+        auto step = [&](int i, uint4 (&rq)[4], uint4 (&rk)[4], uint4 (&rv)[4], float &ar) {
+            const int cn = i + 1;
+            const bool work = cn < n_chunks, refill = cn + 2 < n_chunks;
+            if (i > 0)
+                flush_y(i - 1);
+            if (work) {
+                scan(chunk_len(cn), cn & 1, ar);
+                if (refill)
+                    load_a(cn + 2, ar);
+                stage_qv(cn & 1, rq, rv);
+                if (refill)
+                    load_qv(cn + 2, rq, rv);
+            }
+            wg_barrier();  // a | b
+            if (work) {
+                stage_k(cn & 1, cn & 1, chunk_len(cn), rk);
+                if (refill)
+                    load_k(cn + 2, rk);
+            }
+            wg_barrier();  // chunk i done
+        };
+
+        // prologue: chunk 0 staged whole, chunks 1 and 2 in flight
+        load_qv(0, rq0, rv0);
+        load_k(0, rk0);
+        load_a(0, ar0);
+        if (n_chunks > 1) {
+            load_qv(1, rq1, rv1);
+            load_k(1, rk1);
+            load_a(1, ar1);
+        }
+        scan(chunk_len(0), 0, ar0);
+        if (n_chunks > 2)
+            load_a(2, ar0);
+        wg_barrier();
+        stage_qv(0, rq0, rv0);
+        if (n_chunks > 2)
+            load_qv(2, rq0, rv0);
+        stage_k(0, 0, chunk_len(0), rk0);
+        if (n_chunks > 2)
+            load_k(2, rk0);
+        wg_barrier();
+
+        for (int i = 0; i < n_chunks; i += 2) {
+            step(i, rq1, rk1, rv1, ar1);  // stages chunk i + 1 (odd)
+            if (i + 1 < n_chunks)
+                step(i + 1, rq0, rk0, rv0, ar0);  // stages chunk i + 2 (even)
+        }
+        flush_y(n_chunks - 1);  // the last chunk's y, complete since the last barrier
+        return;
+    }
+
+    // ================================================================ consumers
+    bf16x8 ones;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        ones[s] = static_cast<bf16>(1.f);
+    // wave w owns value columns c = 16w + lr of S (tile tf holds rows f = 16tf + 4lg4 + r)
+    // and features f = 16w + 4lg4 + r of z
+    f32x4 sacc[8];
+    f32x4 zr;
+    const int cw = wave * 16 + lr;
+    const int fw = wave * 16 + lg4 * 4;
+    {
+        const float *Sin = a.nseg == 1 ? a.S + head * kD * kD : slot_ptr(a, head, seg);
+        const float *zin = a.nseg == 1 ? a.z + head * kD : Sin + kD * kD;
+#pragma unroll
+        for (int tf = 0; tf < 8; ++tf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sacc[tf][r] = Sin[(tf * 16 + lg4 * 4 + r) * kD + cw];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zr[r] = zin[fw + r];
+        if (tid < kD)
+            sm.zs[0][tid] = zin[tid];
+    }
+    // transposing-load addresses: this lane supplies 4 adjacent columns (4 (lr & 3) ..)
+    // of token row e = lr >> 2 of its group's set
+    const int te = lr >> 2, tc = 4 * (lr & 3);
+    wg_barrier();
+    wg_barrier();
+
+    for (int i = 0; i < n_chunks; ++i) {
+        const int buf = i & 1;
+        const int n = chunk_len(i);
+        const bf16 *Qb = sm.Qs[buf];
+        const bf16 *Kb = sm.Ks[buf];
+        const bf16 *Vb = sm.Vs[buf];
+        const bf16 *Wb = GATED ? sm.Kw[buf] : sm.Ks[buf];
+
+        // ---- part a: scores (1), then (2) for all four token tiles
+        for (int k = wave; k < G::NPT; k += 8) {
+            int tj = 0;
+            while ((tj + 1) * (tj + 2) / 2 <= k)
+                ++tj;
+            const int ti = k - tj * (tj + 1) / 2;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kf = 0; kf < 4; ++kf) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Kb[pr_off(ti * 16 + sigma(lr), kf * 32 + lg4 * 8)]);
+                const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&Qb[pr_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
+                acc = mfma(ka, qb, acc);
+            }
+            // acc[r] = score (j = 16tj + lr, i = 16ti + sigma(4lg4 + r))
+            const int j = tj * 16 + lr;
+            bf16x4 pk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ii = ti * 16 + sigma(lg4 * 4 + r);
+                float v = ii <= j ? acc[r] : 0.f;
+                if (GATED && ii <= j)
+                    v *= pair_decay(buf, j, ii);
+                pk[r] = static_cast<bf16>(v);
+            }
+            sm.P[k * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
+        }
+        // waves 4-7: phi(q_j) . z_prev for the token tile tj = wave - 4, with z_prev
+        // spread over 16 identical columns
+        if (wave >= 4) {
+            const int j = (wave - 4) * 16 + lr;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kf = 0; kf < 4; ++kf) {
+                const f32x4 zlo = *reinterpret_cast<const f32x4 *>(&sm.zs[buf][kf * 32 + lg4 * 4]);
+                const f32x4 zhi = *reinterpret_cast<const f32x4 *>(&sm.zs[buf][kf * 32 + 16 + lg4 * 4]);
+                bf16x8 zb;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    zb[r] = static_cast<bf16>(zlo[r]);
+                    zb[4 + r] = static_cast<bf16>(zhi[r]);
+                }
+                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, kf * 32 + lg4 * 4)]);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, kf * 32 + 16 + lg4 * 4)]);
+                d = mfma(zb, cat8(lo, hi), d);
+            }
+            if (lg4 == 0)
+                sm.dq[j] = d[0];
+        }
+        f32x4 acc[G::NTJ];
+#pragma unroll
+        for (int tj = 0; tj < G::NTJ; ++tj)
+            acc[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kf = 0; kf < 4; ++kf) {
+            // K step kf: feature tiles 2kf and 2kf+1 of S_prev in bf16; their accumulator
+            // rows 4lg4..4lg4+3 give the permuted k order used on both sides
+            bf16x8 sb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sb[r] = static_cast<bf16>(sacc[2 * kf][r]);
+                sb[4 + r] = static_cast<bf16>(sacc[2 * kf + 1][r]);
+            }
+#pragma unroll
+            for (int tj = 0; tj < G::NTJ; ++tj) {
+                const int j = tj * 16 + lr;
+                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, kf * 32 + lg4 * 4)]);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, kf * 32 + 16 + lg4 * 4)]);
+                acc[tj] = mfma(sb, cat8(lo, hi), acc[tj]);
+            }
+        }
+        wg_barrier();  // a | b
+
+        // ---- part b: (3) with V^T in the score tiles' k order (tokens sigma(4lg4 + e)
+        //      and 16 + sigma(4lg4 + e) of the 32-token step), outputs, then (4)
+#pragma unroll
+        for (int tj = 0; tj < G::NTJ; ++tj) {
+            const int j = tj * 16 + lr;
+            // only element 0 of the denominator accumulator is read
+            f32x4 dac = {sm.dq[j], 0.f, 0.f, 0.f};
+            if (GATED) {
+                const float g = sm.gj[buf][j];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[tj][r] *= g;
+                dac[0] *= g;
+            }
+#pragma unroll
+            for (int ki = 0; 2 * ki <= tj; ++ki) {
+                const int k1 = tj * (tj + 1) / 2 + 2 * ki;
+                const uint2 p1 = sm.P[k1 * 64 + lane];
+                const uint2 p2 = 2 * ki + 1 <= tj ? sm.P[(k1 + 1) * 64 + lane] : make_uint2(0u, 0u);
+                const bf16x8 pb = cat8(__builtin_bit_cast(bf16x4, p1), __builtin_bit_cast(bf16x4, p2));
+                const int tb = ki * 32 + sigma(lg4 * 4 + te);
+                const bf16x8 va = cat8(ld_tr(&Vb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Vb[pr_off(tb + 16, wave * 16 + tc)]));
+                acc[tj] = mfma(va, pb, acc[tj]);
+                dac = mfma(ones, pb, dac);
+            }
+            const float inv = __builtin_amdgcn_rcpf(dac[0] + a.eps);
+            bf16x4 yb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                yb[r] = static_cast<bf16>(acc[tj][r] * inv);
+            *reinterpret_cast<bf16x4 *>(&sm.Ys[ys_off(j, fw)]) = yb;
+        }
+        const float g_end = GATED ? sm.gj[buf][n - 1] : 1.f;
+        if (GATED) {
+#pragma unroll
+            for (int tf = 0; tf < 8; ++tf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sacc[tf][r] *= g_end;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                zr[r] *= g_end;
+        }
+        // (4) in k order: lane group lg4 takes tokens 8lg4 + 2e (first load) and
+        //     8lg4 + 2e + 1 (second) of each 32-token step, alike for both operands
+#pragma unroll
+        for (int ki = 0; ki < G::NKI; ++ki) {
+            const int tb = ki * 32 + lg4 * 8 + 2 * te;
+            const bf16x8 vb = cat8(ld_tr(&Vb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Vb[pr_off(tb + 1, wave * 16 + tc)]));
+#pragma unroll
+            for (int tf = 0; tf < 8; ++tf) {
+                const bf16x8 ka = cat8(ld_tr(&Wb[pr_off(tb, tf * 16 + tc)]), ld_tr(&Wb[pr_off(tb + 1, tf * 16 + tc)]));
+                sacc[tf] = mfma(ka, vb, sacc[tf]);
+            }
+            const bf16x8 kz = cat8(ld_tr(&Wb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Wb[pr_off(tb + 1, wave * 16 + tc)]));
+            zr = mfma(kz, ones, zr);
+        }
+        if (lr == 0)
+            *reinterpret_cast<f32x4 *>(&sm.zs[buf ^ 1][fw]) = zr;
+        wg_barrier();  // chunk i done
+    }
+
+    if (seg != a.nseg - 1)
+        return;
+    float *Sout = a.S + head * kD * kD;
+    float *zout = a.z + head * kD;
+#pragma unroll
+    for (int tf = 0; tf < 8; ++tf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Sout[(tf * 16 + lg4 * 4 + r) * kD + cw] = sacc[tf][r];
+    if (lr == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zout[fw + r] = zr[r];
+    }
 }
 
 // Pass 2: entering state of every segment, in place over the segment maps.
@@ -663,7 +1057,10 @@ hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
         if (e != hipSuccess)
             return e;
     }
-    chunk_kernel<C, GATED, false><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
+    if constexpr (C == kPcC)
+        prefill_pc_kernel<GATED><<<dim3(blocks), dim3(kPcThreads), 0, stream>>>(a);
+    else
+        chunk_kernel<C, GATED, false><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
     return hipGetLastError();
 }
 

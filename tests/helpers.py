@@ -17,6 +17,10 @@ import oracle
 F32_REL = 1e-4          # fp32 inputs: outputs and final S/z
 BF16_Y_ABS = 2e-2       # bf16 inputs: outputs
 BF16_STATE_REL = 1e-2   # bf16 inputs: final S/z
+BF16_U = 2.0 ** -8      # unit roundoff of bf16 under round-to-nearest
+# z sums the bf16-rounded write weights w phi(k) that also feed S; every term is
+# positive, so z's relative error is at most BF16_U plus the fp32 accumulation
+Z_SUM_REL = BF16_U + 6e-4
 
 
 def to_f64(t) -> np.ndarray:

@@ -19,7 +19,7 @@ import oracle
 import recurrent_state_chunkwise_amd as la
 from recurrent_state_chunkwise_amd import workloads as wl
 
-from helpers import BF16_STATE_REL, BF16_Y_ABS, elem_rel, max_abs, maxnorm_rel, to_f64
+from helpers import BF16_STATE_REL, BF16_Y_ABS, Z_SUM_REL, elem_rel, max_abs, maxnorm_rel, to_f64
 
 pytestmark = pytest.mark.gpu
 THREADS = min(16, len(os.sched_getaffinity(0)))
@@ -72,7 +72,7 @@ def test_prefill_full_config(torch, name):
     sr, zrel = maxnorm_rel(to_f64(S), Sr, 2), elem_rel(to_f64(z), zr)
     _report(cfg.name, ya, yr, sr, zrel)
     assert ya <= BF16_Y_ABS and sr <= BF16_STATE_REL and zrel <= BF16_STATE_REL
-    assert yr <= 2e-2 and sr <= 5e-3 and zrel <= 1e-5
+    assert yr <= 2e-2 and sr <= 5e-3 and zrel <= Z_SUM_REL
 
 
 def test_prefill_long_sampled_heads(torch):
@@ -94,7 +94,7 @@ def test_prefill_long_sampled_heads(torch):
             break
         print("  tokens [%6d, %6d): max |dy| %.3e  min den %.3e" % (lo, hi, err[lo:hi].max(), den[:, lo:hi].min()))
     assert ya <= BF16_Y_ABS and sr <= BF16_STATE_REL and zrel <= BF16_STATE_REL
-    assert yr <= 2e-2 and sr <= 5e-3 and zrel <= 1e-5
+    assert yr <= 2e-2 and sr <= 5e-3 and zrel <= Z_SUM_REL
 
 
 def test_decode_full_config_sampled(torch):
@@ -117,7 +117,7 @@ def test_decode_full_config_sampled(torch):
     # the seeding itself against the oracle (fp64 sum of the same 256 writes)
     _, Ss, zs, _ = oracle.recurrence_heads(to_f64(ks[pick_t, 0]), to_f64(ks[pick_t, 0]), to_f64(vs[pick_t, 0]),
                                            eps=cfg.eps, threads=THREADS)
-    assert maxnorm_rel(S_seed, Ss, 2) <= 5e-3 and elem_rel(z_seed, zs) <= 1e-5
+    assert maxnorm_rel(S_seed, Ss, 2) <= 5e-3 and elem_rel(z_seed, zs) <= Z_SUM_REL
     del ks, vs
     y = torch.empty((N, cfg.dv), device="cuda", dtype=torch.bfloat16)
     qh, kh, vh, yh = [], [], [], []
