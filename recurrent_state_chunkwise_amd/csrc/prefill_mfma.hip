@@ -115,11 +115,11 @@ struct Cfg {
 // (KwT: features x tokens, VT: values x tokens) are the K-contiguous operands of the
 // contractions over tokens.  16-byte granules are XOR-swizzled per row so that the
 // 16 rows read by one MFMA operand land in distinct banks.
-template <int C, bool SUMMARY>
+template <int C>
 struct alignas(16) Smem {
     typedef Cfg<C> G;
-    static constexpr int QN = SUMMARY ? 1 : C * kD;
-    static constexpr int PN = SUMMARY ? 1 : G::NPT;
+    static constexpr int QN = C * kD;
+    static constexpr int PN = G::NPT;
     alignas(16) bf16 Qs[QN];         // phi(q) rows
     alignas(16) bf16 Ks[QN];         // phi(k) rows
     alignas(16) bf16 KwT[kD * C];    // w phi(k), token-major
@@ -163,13 +163,14 @@ __device__ __forceinline__ float *slot_ptr(const Args &a, int64_t head, int p)
     return reinterpret_cast<float *>(a.Y + (head * a.T + (int64_t)p * a.seg_len) * kD);
 }
 
-// SUMMARY: pass 1 (segment map from a zero state, written to the next segment's slot).
-// FULL:    pass 3 (outputs from the entering state; the last segment writes S, z).
-template <int C, bool GATED, bool SUMMARY>
+// Pass 3 with 8 waves that stage and multiply in turn (the form used at chunk 128,
+// where two buffers of every tile do not fit in LDS): outputs from the entering state;
+// the last segment writes S, z.
+template <int C, bool GATED>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 {
     typedef Cfg<C> G;
-    __shared__ Smem<C, SUMMARY> sm;
+    __shared__ Smem<C> sm;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -179,8 +180,6 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 
     const int64_t head = blockIdx.x / a.nseg;
     const int seg = blockIdx.x % a.nseg;
-    if (SUMMARY && seg == a.nseg - 1)
-        return;  // the last segment's map is never needed
     const int64_t s0 = (int64_t)seg * a.seg_len;
     const int64_t s1 = seg == a.nseg - 1 ? a.T : s0 + a.seg_len;
     const int64_t len = s1 - s0;
@@ -207,12 +206,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
     f32x4 zr;
     const int cw = wave * 16 + lr;
     const int fw = wave * 16 + lg4 * 4;
-    if (SUMMARY) {
-#pragma unroll
-        for (int tf = 0; tf < 8; ++tf)
-            sacc[tf] = f32x4{0.f, 0.f, 0.f, 0.f};
-        zr = f32x4{0.f, 0.f, 0.f, 0.f};
-    } else {
+    {
         const float *Sin = a.nseg == 1 ? a.S + head * kD * kD : slot_ptr(a, head, seg);
         const float *zin = a.nseg == 1 ? a.z + head * kD : Sin + kD * kD;
 #pragma unroll
@@ -226,7 +220,6 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
         if (tid < kD)
             sm.zs[0][tid] = zin[tid];
     }
-    float g_seg = 1.f;  // product of all gates of the segment (SUMMARY)
 
     // ---------------------------------------------------------------- loads
     // every thread stages TPT consecutive tokens of one 8-wide granule of Q, K and V:
@@ -246,8 +239,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
         const int off = chunk * C * kD * 2 + ld_off;
 #pragma unroll
         for (int p = 0; p < G::TPT; ++p) {
-            if (!SUMMARY)
-                raw_q[p] = bload16(rQ, off + p * kD * 2);
+            raw_q[p] = bload16(rQ, off + p * kD * 2);
             raw_v[p] = bload16(rV, off + p * kD * 2);
         }
     };
@@ -315,8 +307,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                 if (GATED)
                     x[s] = w * f;
             }
-            if (!SUMMARY)
-                *reinterpret_cast<bf16x8 *>(&sm.Ks[qk_off(j, fg * 8)]) = kb;
+            *reinterpret_cast<bf16x8 *>(&sm.Ks[qk_off(j, fg * 8)]) = kb;
             uint4 u;
             if (GATED) {
                 bf16x8 kwb;
@@ -494,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
             const bf16x8 kz = *reinterpret_cast<const bf16x8 *>(&sm.KwT[tm_off<C>(wave * 16 + lr, ki * 32 + lg4 * 8)]);
             zr = mfma(kz, ones, zr);
         }
-        if (!SUMMARY && lr == 0)
+        if (lr == 0)
             *reinterpret_cast<f32x4 *>(&sm.zs[znext][fw]) = zr;
     };
 
@@ -512,8 +503,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
         const bool more = c + 1 < n_chunks;
 
         stage_k(n, gs);
-        if (!SUMMARY)
-            stage_q();
+        stage_q();
         stage_v();
         if (more) {
             prefetch_k(c + 1);
@@ -522,14 +512,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
         }
         __syncthreads();  // A: chunk staged
 
-        if (!SUMMARY) {
-            scores(gs);
-            __syncthreads();  // B: score tiles ready
-            outputs(gs, t0, c & 1);
-        }
+        scores(gs);
+        __syncthreads();  // B: score tiles ready
+        outputs(gs, t0, c & 1);
         const float g_end = GATED ? sm.gj[gs][n - 1] : 1.f;
-        if (GATED)
-            g_seg *= g_end;
         state_write(g_end, (c + 1) & 1);
         if (more)
             gate_scan(chunk_len(c + 1), gs ^ 1);
@@ -537,18 +523,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
     }
 
     // ---------------------------------------------------------------- leaving state
-    float *Sout, *zout;
-    if (SUMMARY) {
-        Sout = slot_ptr(a, head, seg + 1);
-        zout = Sout + kD * kD;
-        if (tid == 0)
-            Sout[kD * kD + kD] = g_seg;
-    } else {
-        if (seg != a.nseg - 1)
-            return;
-        Sout = a.S + head * kD * kD;
-        zout = a.z + head * kD;
-    }
+    if (seg != a.nseg - 1)
+        return;
+    float *Sout = a.S + head * kD * kD;
+    float *zout = a.z + head * kD;
 #pragma unroll
     for (int tf = 0; tf < 8; ++tf)
 #pragma unroll
@@ -650,6 +628,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
     const int64_t s1 = seg == a.nseg - 1 ? a.T : s0 + a.seg_len;
     const int64_t len = s1 - s0;
     const int n_chunks = (int)((len + C - 1) / C);
+    const int n_steps = (n_chunks + 1) & ~1;  // both roles walk an even number of chunk steps
     auto chunk_len = [&](int c) { return (int)min((int64_t)C, len - (int64_t)c * C); };
     const int64_t row0 = head * a.T + s0;
 
@@ -685,8 +664,8 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
             for (int p = 0; p < 4; ++p)
                 rk[p] = bload16(rK, c * C * kD * 2 + ld_off + p * kD * 2);
         };
-        auto load_a = [&](int c, float &ar) {
-            if (GATED && scanner)
+        auto load_a = [&](int c, float &ar) {  // every producer wave loads; the scanner uses it
+            if (GATED)
                 ar = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (c * C + lane) * 4, 0, 0));
         };
         // inclusive scans of log(alpha) and of the last zero-gate position (one wave)
@@ -767,25 +746,23 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         };
         // one chunk interval: write out y of chunk i - 1, stage chunk cn = i + 1 from its
         // register set, then refill that set with chunk cn + 2
+        // Loads and stores past the end of the segment read zeros or are dropped by the
+        // buffer resources; they are issued unconditionally so that every wait on them is
+        // a counted one.  Step 0 flushes to chunk n_chunks, which is such a store.
         auto step = [&](int i, uint4 (&rq)[4], uint4 (&rk)[4], uint4 (&rv)[4], float &ar) {
             const int cn = i + 1;
-            const bool work = cn < n_chunks, refill = cn + 2 < n_chunks;
-            if (i > 0)
-                flush_y(i - 1);
-            if (work) {
+            const bool work = cn < n_chunks;
+            flush_y(i > 0 ? i - 1 : n_chunks);
+            if (work)
                 scan(chunk_len(cn), cn & 1, ar);
-                if (refill)
-                    load_a(cn + 2, ar);
+            load_a(cn + 2, ar);
+            if (work)
                 stage_qv(cn & 1, rq, rv);
-                if (refill)
-                    load_qv(cn + 2, rq, rv);
-            }
+            load_qv(cn + 2, rq, rv);
             wg_barrier();  // a | b
-            if (work) {
+            if (work)
                 stage_k(cn & 1, cn & 1, chunk_len(cn), rk);
-                if (refill)
-                    load_k(cn + 2, rk);
-            }
+            load_k(cn + 2, rk);
             wg_barrier();  // chunk i done
         };
 
@@ -793,29 +770,25 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         load_qv(0, rq0, rv0);
         load_k(0, rk0);
         load_a(0, ar0);
-        if (n_chunks > 1) {
-            load_qv(1, rq1, rv1);
-            load_k(1, rk1);
-            load_a(1, ar1);
-        }
+        load_qv(1, rq1, rv1);
+        load_k(1, rk1);
+        load_a(1, ar1);
         scan(chunk_len(0), 0, ar0);
-        if (n_chunks > 2)
-            load_a(2, ar0);
+        load_a(2, ar0);
         wg_barrier();
         stage_qv(0, rq0, rv0);
-        if (n_chunks > 2)
-            load_qv(2, rq0, rv0);
+        load_qv(2, rq0, rv0);
         stage_k(0, 0, chunk_len(0), rk0);
-        if (n_chunks > 2)
-            load_k(2, rk0);
+        load_k(2, rk0);
         wg_barrier();
 
-        for (int i = 0; i < n_chunks; i += 2) {
-            step(i, rq1, rk1, rv1, ar1);  // stages chunk i + 1 (odd)
-            if (i + 1 < n_chunks)
-                step(i + 1, rq0, rk0, rv0, ar0);  // stages chunk i + 2 (even)
+        for (int i = 0; i < n_steps; i += 2) {
+            step(i, rq1, rk1, rv1, ar1);      // stages chunk i + 1 (odd)
+            step(i + 1, rq0, rk0, rv0, ar0);  // stages chunk i + 2 (even)
         }
-        flush_y(n_chunks - 1);  // the last chunk's y, complete since the last barrier
+        // the last chunk's y, complete since the last barrier (already written by the
+        // trailing empty step when the chunk count is odd)
+        flush_y(n_steps == n_chunks ? n_chunks - 1 : n_chunks);
         return;
     }
 
@@ -850,7 +823,12 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
     wg_barrier();
     wg_barrier();
 
-    for (int i = 0; i < n_chunks; ++i) {
+    for (int i = 0; i < n_steps; ++i) {
+        if (i >= n_chunks) {  // the trailing empty step of an odd chunk count
+            wg_barrier();
+            wg_barrier();
+            break;
+        }
         const int buf = i & 1;
         const int n = chunk_len(i);
         const bf16 *Qb = sm.Qs[buf];
@@ -1008,6 +986,209 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
     }
 }
 
+// ============================================================================ pass 1, chunk 64
+// Segment maps in the same producer / consumer form: producers stage the write weights
+// w phi(k) and V of the next chunk as token rows, consumers fold each chunk into
+// (S, z) with transposing loads, one workgroup barrier per chunk.  The gate scan runs
+// two chunks ahead of the consumers, so its results are kept for three chunks.
+template <bool GATED>
+struct alignas(16) SumSmem {
+    alignas(16) bf16 Ws[2][kPcC * kRow];  // w phi(k) (ungated: phi(k), zero past the end)
+    alignas(16) bf16 Vs[2][kPcC * kRow];
+    alignas(16) float lg[3][kPcC];
+    alignas(16) float gj[3][kPcC];
+    alignas(16) int zp[3][kPcC];
+};
+
+template <bool GATED>
+__global__ __launch_bounds__(kPcThreads) void summary_pc_kernel(Args a)
+{
+    constexpr int C = kPcC;
+    typedef Cfg<C> G;
+    __shared__ SumSmem<GATED> sm;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int lr = lane & 15;
+    const int lg4 = lane >> 4;
+
+    const int64_t head = blockIdx.x / a.nseg;
+    const int seg = blockIdx.x % a.nseg;
+    if (seg == a.nseg - 1)
+        return;  // the last segment's map is never needed
+    const int64_t s0 = (int64_t)seg * a.seg_len;
+    const int64_t len = a.seg_len;
+    const int n_chunks = (int)((len + C - 1) / C);
+    const int n_steps = (n_chunks + 1) & ~1;  // both roles walk an even number of chunk steps
+    auto chunk_len = [&](int c) { return (int)min((int64_t)C, len - (int64_t)c * C); };
+    const int64_t row0 = head * a.T + s0;
+
+    if (wave >= 8) {
+        // ============================================================ producers
+        const rsrc_t rK = make_rsrc(a.K + row0 * kD, len * kD * 2);
+        const rsrc_t rV = make_rsrc(a.V + row0 * kD, len * kD * 2);
+        const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
+        const int pt = tid - kPcConsumers;
+        const bool scanner = wave == 8;
+        const int fg = pt & 15, tg = pt >> 4;  // granule fg of tokens 4tg .. 4tg + 3
+        const int ld_off = tg * 4 * kD * 2 + fg * 16;
+        uint4 rk0[4], rv0[4], rk1[4], rv1[4];
+        float ar0 = 0.f, ar1 = 0.f;  // alpha of even / odd chunks
+
+        auto load_kv = [&](int c, uint4 (&rk)[4], uint4 (&rv)[4]) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                rk[p] = bload16(rK, c * C * kD * 2 + ld_off + p * kD * 2);
+                rv[p] = bload16(rV, c * C * kD * 2 + ld_off + p * kD * 2);
+            }
+        };
+        auto load_a = [&](int c, float &ar) {  // every producer wave loads; the scanner uses it
+            if (GATED)
+                ar = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (c * C + lane) * 4, 0, 0));
+        };
+        auto scan = [&](int n, int gs, float ar) {
+            if (GATED && scanner) {
+                const float av = lane < n ? ar : 1.f;
+                float s = av > 0.f ? __logf(av) : 0.f;
+                int zf = av == 0.f ? lane : -1;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float s2 = __shfl_up(s, off, 64);
+                    const int z2 = __shfl_up(zf, off, 64);
+                    if (lane >= off) {
+                        s += s2;
+                        zf = max(zf, z2);
+                    }
+                }
+                sm.lg[gs][lane] = s;
+                sm.zp[gs][lane] = zf;
+                sm.gj[gs][lane] = zf >= 0 ? 0.f : __expf(s);
+            }
+        };
+        auto stage = [&](int buf, int gs, int n, const uint4 (&rk)[4], const uint4 (&rv)[4]) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int j = tg * 4 + p;
+                const float w = j >= n ? 0.f
+                                       : (GATED ? (sm.zp[gs][n - 1] > j ? 0.f : __expf(sm.lg[gs][n - 1] - sm.lg[gs][j]))
+                                                : 1.f);
+                float x[8];
+                unpack8(rk[p], x);
+                bf16x8 kb;
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    kb[s] = static_cast<bf16>(GATED ? w * phi(x[s]) : phi(x[s]));
+                uint4 u = *reinterpret_cast<uint4 *>(&kb);
+                if (!GATED && j >= n)
+                    u = make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4 *>(&sm.Ws[buf][pr_off(j, fg * 8)]) = u;
+                *reinterpret_cast<uint4 *>(&sm.Vs[buf][pr_off(j, fg * 8)]) = rv[p];
+            }
+        };
+        // interval i: stage chunk i + 1 from its set and refill the set with chunk i + 3;
+        // scan the gates of chunk i + 2 and load the alpha of chunk i + 4 in its place.
+        // Loads past the end of the segment read zeros through the buffer resource; they
+        // are issued unconditionally so that every wait on them is a counted one.
+        auto step = [&](int i, uint4 (&rk)[4], uint4 (&rv)[4], float &ar) {
+            const int cn = i + 1;
+            if (cn < n_chunks)
+                stage(cn & 1, cn % 3, chunk_len(cn), rk, rv);
+            load_kv(cn + 2, rk, rv);
+            if (i + 2 < n_chunks)
+                scan(chunk_len(i + 2), (i + 2) % 3, ar);
+            load_a(i + 4, ar);
+            wg_barrier();  // chunk i done, chunk i + 1 staged
+        };
+
+        load_kv(0, rk0, rv0);
+        load_a(0, ar0);
+        load_kv(1, rk1, rv1);
+        load_a(1, ar1);
+        scan(chunk_len(0), 0, ar0);
+        if (n_chunks > 1)
+            scan(chunk_len(1), 1, ar1);
+        load_a(2, ar0);
+        load_a(3, ar1);
+        wg_barrier();
+        stage(0, 0, chunk_len(0), rk0, rv0);
+        load_kv(2, rk0, rv0);
+        wg_barrier();
+        for (int i = 0; i < n_steps; i += 2) {
+            step(i, rk1, rv1, ar0);  // stages chunk i + 1 (odd), scans chunk i + 2 (even)
+            step(i + 1, rk0, rv0, ar1);
+        }
+        return;
+    }
+
+    // ================================================================ consumers
+    bf16x8 ones;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        ones[s] = static_cast<bf16>(1.f);
+    f32x4 sacc[8];
+#pragma unroll
+    for (int tf = 0; tf < 8; ++tf)
+        sacc[tf] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 zr = {0.f, 0.f, 0.f, 0.f};
+    float g_seg = 1.f;
+    const int cw = wave * 16 + lr;
+    const int fw = wave * 16 + lg4 * 4;
+    const int te = lr >> 2, tc = 4 * (lr & 3);
+    wg_barrier();
+    wg_barrier();
+    for (int i = 0; i < n_steps; ++i) {
+        if (i >= n_chunks) {  // the trailing empty step of an odd chunk count
+            wg_barrier();
+            break;
+        }
+        const int buf = i & 1;
+        const bf16 *Wb = sm.Ws[buf];
+        const bf16 *Vb = sm.Vs[buf];
+        if (GATED) {
+            const float g_end = sm.gj[i % 3][chunk_len(i) - 1];
+            g_seg *= g_end;
+#pragma unroll
+            for (int tf = 0; tf < 8; ++tf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sacc[tf][r] *= g_end;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                zr[r] *= g_end;
+        }
+#pragma unroll
+        for (int ki = 0; ki < G::NKI; ++ki) {
+            const int tb = ki * 32 + lg4 * 8 + 2 * te;
+            const bf16x8 vb = cat8(ld_tr(&Vb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Vb[pr_off(tb + 1, wave * 16 + tc)]));
+#pragma unroll
+            for (int tf = 0; tf < 8; ++tf) {
+                const bf16x8 ka = cat8(ld_tr(&Wb[pr_off(tb, tf * 16 + tc)]), ld_tr(&Wb[pr_off(tb + 1, tf * 16 + tc)]));
+                sacc[tf] = mfma(ka, vb, sacc[tf]);
+            }
+            const bf16x8 kz = cat8(ld_tr(&Wb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Wb[pr_off(tb + 1, wave * 16 + tc)]));
+            zr = mfma(kz, ones, zr);
+        }
+        wg_barrier();  // chunk i folded
+    }
+
+    // the map goes to the next segment's slot: S, z, then the product of the gates
+    float *Sout = slot_ptr(a, head, seg + 1);
+    float *zout = Sout + kD * kD;
+    if (tid == 0)
+        Sout[kD * kD + kD] = g_seg;
+#pragma unroll
+    for (int tf = 0; tf < 8; ++tf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Sout[(tf * 16 + lg4 * 4 + r) * kD + cw] = sacc[tf][r];
+    if (lr == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zout[fw + r] = zr[r];
+    }
+}
+
 // Pass 2: entering state of every segment, in place over the segment maps.
 // slot 0 <- (S0, z0); slot p <- G_{p-1} slot(p-1) + dS_{p-1}   (p = 1 .. nseg-1)
 // The maps are read 8 at a time before the chain runs, so the loads overlap.
@@ -1045,10 +1226,9 @@ hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)(n_heads * a.nseg);
     if (a.nseg > 1) {
-        // pass 1 walks 128-token chunks whatever the caller's chunk: its chunking only
-        // changes the rounding of the segment maps, and longer chunks keep more bytes
-        // in flight
-        chunk_kernel<128, GATED, true><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
+        // pass 1 walks 64-token chunks whatever the caller's chunk: its chunking only
+        // changes the rounding of the segment maps
+        summary_pc_kernel<GATED><<<dim3(blocks), dim3(kPcThreads), 0, stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -1060,7 +1240,7 @@ hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
     if constexpr (C == kPcC)
         prefill_pc_kernel<GATED><<<dim3(blocks), dim3(kPcThreads), 0, stream>>>(a);
     else
-        chunk_kernel<C, GATED, false><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
+        chunk_kernel<C, GATED><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
     return hipGetLastError();
 }
 
