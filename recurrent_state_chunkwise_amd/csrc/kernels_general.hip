@@ -323,21 +323,24 @@ hipError_t launch_general_typed(const PrefillArgs &a, hipStream_t stream)
 }
 
 // ===================================================================== decode
-// d = dv = 128: one workgroup of 256 threads per state.  Thread (rg, cg) owns
-// VEC consecutive columns (cg) of the rows rg, rg + NRG, ..., so each wave reads
-// adjacent full rows; all of a thread's rows are loaded before any is used.
+constexpr int kDecodeThreads = 512;
+
+// d = dv = 128: one workgroup of 512 threads per state (measured faster than 256 or
+// 1024 on this streaming update).  Thread (rg, cg) owns VEC consecutive columns (cg)
+// of the rows rg, rg + NRG, ..., so each wave reads adjacent full rows; all of a
+// thread's rows are loaded before any is used.
 // Each state is touched once per step, so its loads and stores are marked
 // non-temporal to keep it from displacing other lines in the caches.
 template <typename TI, typename TA, int VEC>
-__global__ __launch_bounds__(kThreads) void decode_w128_kernel(
+__global__ __launch_bounds__(kDecodeThreads) void decode_w128_kernel(
     const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v, const TA *__restrict__ alpha,
     TA eps, TI *__restrict__ y, TA *__restrict__ S, TA *__restrict__ z)
 {
-    constexpr int D = 128, DV = 128, NCG = DV / VEC, NRG = kThreads / NCG, ROWS = D / NRG;
+    constexpr int D = 128, DV = 128, NCG = DV / VEC, NRG = kDecodeThreads / NCG, ROWS = D / NRG;
     typedef TA vec_t __attribute__((ext_vector_type(VEC)));
     __shared__ TA kf[D], qf[D], vs[DV];
     __shared__ TA red[NRG][DV];
-    __shared__ TA dred[kThreads / 64];
+    __shared__ TA dred[kDecodeThreads / 64];
 
     const int tid = threadIdx.x;
     const int64_t n = blockIdx.x;
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void decode_w128_kernel(
             num += red[r][tid];
         TA den = TA(0);
 #pragma unroll
-        for (int w = 0; w < kThreads / 64; ++w)
+        for (int w = 0; w < kDecodeThreads / 64; ++w)
             den += dred[w];
         y[n * DV + tid] = from_acc<TI>(num / (den + eps));
     }
@@ -459,7 +462,7 @@ hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t stream)
     constexpr int VEC = 16 / sizeof(TA);
     const bool aligned = (reinterpret_cast<uintptr_t>(a.S) % 16) == 0;
     if (a.d == 128 && a.dv == 128 && aligned) {
-        decode_w128_kernel<TI, TA, VEC><<<dim3((unsigned)a.n_states), dim3(kThreads), 0, stream>>>(
+        decode_w128_kernel<TI, TA, VEC><<<dim3((unsigned)a.n_states), dim3(kDecodeThreads), 0, stream>>>(
             static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
             static_cast<const TA *>(a.alpha), static_cast<TA>(a.eps), static_cast<TI *>(a.y),
             static_cast<TA *>(a.S), static_cast<TA *>(a.z));
