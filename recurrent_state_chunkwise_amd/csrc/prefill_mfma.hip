@@ -560,9 +560,20 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 // banks as long as each transposing load takes only even or only odd token rows per
 // 32 lanes; the scores therefore feed K~ rows to the MFMA in the order sigma (even
 // tokens first), which makes the score tiles, and so V^T in (3), come in that order.
+// The two score tiles that one K step of (3) needs sit side by side, so that step reads
+// them with one 16-byte load per lane.  Paired 8-byte LDS loads (which the compiler forms
+// from loads a known distance apart) run at half the rate of two single loads on gfx950,
+// so the two 8-byte halves of a (2) operand are kept from being fused.
 constexpr int kPcC = 64;
 constexpr int kPcConsumers = 512;
-constexpr int kPcThreads = 768;
+// producer waves of the output pass (4 or 8); the segment-map pass always has 4
+#ifndef LA_PC_PRODUCERS
+#define LA_PC_PRODUCERS 4
+#endif
+constexpr int kPcProducers = LA_PC_PRODUCERS;
+static_assert(kPcProducers == 4 || kPcProducers == 8, "4 or 8 producer waves");
+constexpr int kPcThreads = kPcConsumers + 64 * kPcProducers;
+constexpr int kSumThreads = kPcConsumers + 256;
 
 constexpr int kRow = kD + 8;  // padded token row, in elements
 __device__ __forceinline__ int pr_off(int row, int col) { return row * kRow + col; }
@@ -580,10 +591,20 @@ __device__ __forceinline__ bf16x4 ld_tr(const bf16 *p)
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
     return __builtin_bit_cast(bf16x4, v);
 }
+// x, hidden from the optimiser (which then cannot fuse loads addressed from it with others)
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi)
 {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
+
+// score tile (tj, ti) lives in half ti & 1 of pair slot kPairBase[tj] + ti / 2
+constexpr int kPairBase[4] = {0, 1, 2, 4};
+constexpr int kPairSlots = 6;
 
 template <bool GATED>
 struct alignas(16) PcSmem {
@@ -591,8 +612,11 @@ struct alignas(16) PcSmem {
     alignas(16) bf16 Ks[2][kPcC * kRow];           // phi(k); ungated, also the write weights
     alignas(16) bf16 Vs[2][kPcC * kRow];           // v
     alignas(16) bf16 Kw[GATED ? 2 : 1][GATED ? kPcC * kRow : 8];  // w phi(k) (gated)
-    alignas(16) bf16 Ys[kPcC * kD];                // y of the last finished chunk, granules XOR-swizzled by row
-    alignas(16) uint2 P[Cfg<kPcC>::NPT * 64];      // bf16 score tiles, one 4-value group per lane
+    // y of the last finished chunk, 16-byte granules XOR-swizzled by row.  Gated, it lives
+    // in that chunk's phi(k) buffer, dead from the scores until the producers stage the
+    // chunk after next into it (after the y of this chunk has gone out).
+    alignas(16) bf16 Ys[GATED ? 8 : kPcC * kD];
+    alignas(16) uint4 P[kPairSlots * 64];          // bf16 score tiles in pairs, 4 values of each per lane
     alignas(16) float zs[2][kD];                   // z entering the chunk, by chunk parity
     alignas(16) float dq[kPcC];                    // phi(q_j) . z_prev
     alignas(16) float lg[2][kPcC];
@@ -645,23 +669,24 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         const rsrc_t rY = make_rsrc(a.Y + row0 * kD, len * kD * 2);
         const int pt = tid - kPcConsumers;
         const bool scanner = wave == 8;
-        // thread (fg, tg) stages granule fg (8 features) of tokens 4tg .. 4tg + 3
+        // thread (fg, tg) stages granule fg (8 features) of tokens TPT tg .. TPT tg + TPT - 1
+        constexpr int TPT = 16 / kPcProducers;
         const int fg = pt & 15, tg = pt >> 4;
-        const int ld_off = tg * 4 * kD * 2 + fg * 16;
+        const int ld_off = tg * TPT * kD * 2 + fg * 16;
         // two register sets: chunk c is loaded into set c & 1 two chunks before it is staged
-        uint4 rq0[4], rk0[4], rv0[4], rq1[4], rk1[4], rv1[4];
+        uint4 rq0[TPT], rk0[TPT], rv0[TPT], rq1[TPT], rk1[TPT], rv1[TPT];
         float ar0 = 0.f, ar1 = 0.f;
 
-        auto load_qv = [&](int c, uint4 (&rq)[4], uint4 (&rv)[4]) {
+        auto load_qv = [&](int c, uint4 (&rq)[TPT], uint4 (&rv)[TPT]) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
+            for (int p = 0; p < TPT; ++p) {
                 rq[p] = bload16(rQ, c * C * kD * 2 + ld_off + p * kD * 2);
                 rv[p] = bload16(rV, c * C * kD * 2 + ld_off + p * kD * 2);
             }
         };
-        auto load_k = [&](int c, uint4 (&rk)[4]) {
+        auto load_k = [&](int c, uint4 (&rk)[TPT]) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
+            for (int p = 0; p < TPT; ++p)
                 rk[p] = bload16(rK, c * C * kD * 2 + ld_off + p * kD * 2);
         };
         auto load_a = [&](int c, float &ar) {  // every producer wave loads; the scanner uses it
@@ -689,10 +714,10 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
             }
         };
         // phi(q) rows and V rows
-        auto stage_qv = [&](int buf, const uint4 (&rq)[4], const uint4 (&rv)[4]) {
+        auto stage_qv = [&](int buf, const uint4 (&rq)[TPT], const uint4 (&rv)[TPT]) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int j = tg * 4 + p;
+            for (int p = 0; p < TPT; ++p) {
+                const int j = tg * TPT + p;
                 float x[8];
                 unpack8(rq[p], x);
                 bf16x8 qb;
@@ -707,10 +732,10 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         // chunk end, 0 past the end of the segment (whose tokens load as zeros).  The
         // ungated weights are phi(k) itself, so those rows of Ks are zeroed instead (the
         // scores never use them: they lie above the diagonal of every kept row).
-        auto stage_k = [&](int buf, int gs, int n, const uint4 (&rk)[4]) {
+        auto stage_k = [&](int buf, int gs, int n, const uint4 (&rk)[TPT]) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int j = tg * 4 + p;
+            for (int p = 0; p < TPT; ++p) {
+                const int j = tg * TPT + p;
                 float x[8];
                 unpack8(rk[p], x);
                 bf16x8 kb, kwb;
@@ -730,15 +755,16 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                     *reinterpret_cast<bf16x8 *>(&sm.Kw[buf][pr_off(j, fg * 8)]) = kwb;
             }
         };
-        // y of chunk c from the LDS tile to HBM as whole 256-byte rows: wave 8 + u takes
-        // rows 16u .. 16u + 15, four rows per store; rows past the end of the segment fall
-        // outside rY and are dropped
+        // y of chunk c from the LDS tile to HBM as whole 256-byte rows: producer wave pw
+        // takes rows 4 TPT pw .. 4 TPT pw + 4 TPT - 1, four rows per store; rows past the end
+        // of the segment fall outside rY and are dropped
         const int pw = wave - 8;
         auto flush_y = [&](int c) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int row = pw * 16 + u * 4 + (lane >> 4), g = lane & 15;
-                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.Ys[row * kD + g * 8]);
+            for (int u = 0; u < TPT; ++u) {
+                const int row = pw * 4 * TPT + u * 4 + (lane >> 4), g = lane & 15;
+                const bf16 *ys = GATED ? sm.Ks[c & 1] : sm.Ys;
+                const uint4 v = *reinterpret_cast<const uint4 *>(&ys[row * kD + g * 8]);
                 const int off = ((c * C + row) * kD + ((g ^ (row & 15)) << 3)) * 2;
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), rY, off, 0, 0);
@@ -749,7 +775,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         // Loads and stores past the end of the segment read zeros or are dropped by the
         // buffer resources; they are issued unconditionally so that every wait on them is
         // a counted one.  Step 0 flushes to chunk n_chunks, which is such a store.
-        auto step = [&](int i, uint4 (&rq)[4], uint4 (&rk)[4], uint4 (&rv)[4], float &ar) {
+        auto step = [&](int i, uint4 (&rq)[TPT], uint4 (&rk)[TPT], uint4 (&rv)[TPT], float &ar) {
             const int cn = i + 1;
             const bool work = cn < n_chunks;
             flush_y(i > 0 ? i - 1 : n_chunks);
@@ -820,6 +846,12 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
     // transposing-load addresses: this lane supplies 4 adjacent columns (4 (lr & 3) ..)
     // of token row e = lr >> 2 of its group's set
     const int te = lr >> 2, tc = 4 * (lr & 3);
+    // the second halves of the pair slots of tiles (0, 0) and (2, 2) hold no tile: zero,
+    // they stand for the tiles above the diagonal in the K steps of (3)
+    if (wave == 0) {
+        reinterpret_cast<uint2 *>(&sm.P[kPairBase[0] * 64 + lane])[1] = make_uint2(0u, 0u);
+        reinterpret_cast<uint2 *>(&sm.P[(kPairBase[2] + 1) * 64 + lane])[1] = make_uint2(0u, 0u);
+    }
     wg_barrier();
     wg_barrier();
 
@@ -860,7 +892,8 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                     v *= pair_decay(buf, j, ii);
                 pk[r] = static_cast<bf16>(v);
             }
-            sm.P[k * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
+            reinterpret_cast<uint2 *>(&sm.P[(kPairBase[tj] + (ti >> 1)) * 64 + lane])[ti & 1] =
+                *reinterpret_cast<uint2 *>(&pk);
         }
         // waves 4-7: phi(q_j) . z_prev for the token tile tj = wave - 4, with z_prev
         // spread over 16 identical columns
@@ -878,7 +911,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                     zb[4 + r] = static_cast<bf16>(zhi[r]);
                 }
                 const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, kf * 32 + lg4 * 4)]);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, kf * 32 + 16 + lg4 * 4)]);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, opaque(kf * 32 + 16 + lg4 * 4))]);
                 d = mfma(zb, cat8(lo, hi), d);
             }
             if (lg4 == 0)
@@ -898,11 +931,12 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 sb[r] = static_cast<bf16>(sacc[2 * kf][r]);
                 sb[4 + r] = static_cast<bf16>(sacc[2 * kf + 1][r]);
             }
+            const int hi_col = opaque(kf * 32 + 16 + lg4 * 4);
 #pragma unroll
             for (int tj = 0; tj < G::NTJ; ++tj) {
                 const int j = tj * 16 + lr;
                 const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, kf * 32 + lg4 * 4)]);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, kf * 32 + 16 + lg4 * 4)]);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, hi_col)]);
                 acc[tj] = mfma(sb, cat8(lo, hi), acc[tj]);
             }
         }
@@ -924,10 +958,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
             }
 #pragma unroll
             for (int ki = 0; 2 * ki <= tj; ++ki) {
-                const int k1 = tj * (tj + 1) / 2 + 2 * ki;
-                const uint2 p1 = sm.P[k1 * 64 + lane];
-                const uint2 p2 = 2 * ki + 1 <= tj ? sm.P[(k1 + 1) * 64 + lane] : make_uint2(0u, 0u);
-                const bf16x8 pb = cat8(__builtin_bit_cast(bf16x4, p1), __builtin_bit_cast(bf16x4, p2));
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, sm.P[(kPairBase[tj] + ki) * 64 + lane]);
                 const int tb = ki * 32 + sigma(lg4 * 4 + te);
                 const bf16x8 va = cat8(ld_tr(&Vb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Vb[pr_off(tb + 16, wave * 16 + tc)]));
                 acc[tj] = mfma(va, pb, acc[tj]);
@@ -938,7 +969,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 yb[r] = static_cast<bf16>(acc[tj][r] * inv);
-            *reinterpret_cast<bf16x4 *>(&sm.Ys[ys_off(j, fw)]) = yb;
+            *reinterpret_cast<bf16x4 *>(&(GATED ? sm.Ks[buf] : sm.Ys)[ys_off(j, fw)]) = yb;
         }
         const float g_end = GATED ? sm.gj[buf][n - 1] : 1.f;
         if (GATED) {
@@ -1001,7 +1032,7 @@ struct alignas(16) SumSmem {
 };
 
 template <bool GATED>
-__global__ __launch_bounds__(kPcThreads) void summary_pc_kernel(Args a)
+__global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
 {
     constexpr int C = kPcC;
     typedef Cfg<C> G;
@@ -1228,7 +1259,7 @@ hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
     if (a.nseg > 1) {
         // pass 1 walks 64-token chunks whatever the caller's chunk: its chunking only
         // changes the rounding of the segment maps
-        summary_pc_kernel<GATED><<<dim3(blocks), dim3(kPcThreads), 0, stream>>>(a);
+        summary_pc_kernel<GATED><<<dim3(blocks), dim3(kSumThreads), 0, stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
