@@ -566,14 +566,19 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 // so the two 8-byte halves of a (2) operand are kept from being fused.
 constexpr int kPcC = 64;
 constexpr int kPcConsumers = 512;
-// producer waves of the output pass (4 or 8); the segment-map pass always has 4
+// producer waves of the output pass (4 or 8)
 #ifndef LA_PC_PRODUCERS
 #define LA_PC_PRODUCERS 4
 #endif
 constexpr int kPcProducers = LA_PC_PRODUCERS;
 static_assert(kPcProducers == 4 || kPcProducers == 8, "4 or 8 producer waves");
 constexpr int kPcThreads = kPcConsumers + 64 * kPcProducers;
-constexpr int kSumThreads = kPcConsumers + 256;
+#ifndef LA_SUM_PRODUCERS
+#define LA_SUM_PRODUCERS 8
+#endif
+constexpr int kSumProducers = LA_SUM_PRODUCERS;  // producer waves of the segment-map pass
+static_assert(kSumProducers == 4 || kSumProducers == 8, "4 or 8 producer waves");
+constexpr int kSumThreads = kPcConsumers + 64 * kSumProducers;
 
 constexpr int kRow = kD + 8;  // padded token row, in elements
 __device__ __forceinline__ int pr_off(int row, int col) { return row * kRow + col; }
@@ -1021,7 +1026,9 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
 // Segment maps in the same producer / consumer form: producers stage the write weights
 // w phi(k) and V of the next chunk as token rows, consumers fold each chunk into
 // (S, z) with transposing loads, one workgroup barrier per chunk.  The gate scan runs
-// two chunks ahead of the consumers, so its results are kept for three chunks.
+// two chunks ahead of the consumers, so its results are kept for three chunks.  This
+// pass has 8 producer waves (16 in all): its consumers only do the state write, so the
+// staging sets the pace, and the registers of both roles fit 4 waves per SIMD.
 template <bool GATED>
 struct alignas(16) SumSmem {
     alignas(16) bf16 Ws[2][kPcC * kRow];  // w phi(k) (ungated: phi(k), zero past the end)
@@ -1062,14 +1069,15 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
         const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
         const int pt = tid - kPcConsumers;
         const bool scanner = wave == 8;
-        const int fg = pt & 15, tg = pt >> 4;  // granule fg of tokens 4tg .. 4tg + 3
-        const int ld_off = tg * 4 * kD * 2 + fg * 16;
-        uint4 rk0[4], rv0[4], rk1[4], rv1[4];
+        constexpr int TPT = 16 / kSumProducers;  // tokens per thread and chunk
+        const int fg = pt & 15, tg = pt >> 4;    // granule fg of tokens TPT tg .. TPT tg + TPT - 1
+        const int ld_off = tg * TPT * kD * 2 + fg * 16;
+        uint4 rk0[TPT], rv0[TPT], rk1[TPT], rv1[TPT];
         float ar0 = 0.f, ar1 = 0.f;  // alpha of even / odd chunks
 
-        auto load_kv = [&](int c, uint4 (&rk)[4], uint4 (&rv)[4]) {
+        auto load_kv = [&](int c, uint4 (&rk)[TPT], uint4 (&rv)[TPT]) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
+            for (int p = 0; p < TPT; ++p) {
                 rk[p] = bload16(rK, c * C * kD * 2 + ld_off + p * kD * 2);
                 rv[p] = bload16(rV, c * C * kD * 2 + ld_off + p * kD * 2);
             }
@@ -1097,10 +1105,10 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                 sm.gj[gs][lane] = zf >= 0 ? 0.f : __expf(s);
             }
         };
-        auto stage = [&](int buf, int gs, int n, const uint4 (&rk)[4], const uint4 (&rv)[4]) {
+        auto stage = [&](int buf, int gs, int n, const uint4 (&rk)[TPT], const uint4 (&rv)[TPT]) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int j = tg * 4 + p;
+            for (int p = 0; p < TPT; ++p) {
+                const int j = tg * TPT + p;
                 const float w = j >= n ? 0.f
                                        : (GATED ? (sm.zp[gs][n - 1] > j ? 0.f : __expf(sm.lg[gs][n - 1] - sm.lg[gs][j]))
                                                 : 1.f);
@@ -1121,7 +1129,7 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
         // scan the gates of chunk i + 2 and load the alpha of chunk i + 4 in its place.
         // Loads past the end of the segment read zeros through the buffer resource; they
         // are issued unconditionally so that every wait on them is a counted one.
-        auto step = [&](int i, uint4 (&rk)[4], uint4 (&rv)[4], float &ar) {
+        auto step = [&](int i, uint4 (&rk)[TPT], uint4 (&rv)[TPT], float &ar) {
             const int cn = i + 1;
             if (cn < n_chunks)
                 stage(cn & 1, cn % 3, chunk_len(cn), rk, rv);
