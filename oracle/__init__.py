@@ -24,6 +24,8 @@ Source of truth is the page "Linear attention：把历史写进状态"
 * :func:`scan_prefix` -- the affine composition (a2, B2) o (a1, B1) =
   (a2 a1, a2 B1 + B2) of section "门控递推为什么能做并行 scan", combined in
   tree order.
+* :func:`delta_steps` -- the delta rule of section "Delta rule：先读旧答案，再写误差"
+  (S <- S + beta k (v - S^T k), read y = S^T q after the write), also in C.
 
 Every function here is pinned by the CPU tests against the page's worked
 examples, closed forms and brute force (see ``tests/test_oracle_pins.py``).
@@ -79,6 +81,9 @@ def _load():
                                               dp, dp, dp, dp]
             lib.oracle_phi.restype = ctypes.c_double
             lib.oracle_phi.argtypes = [ctypes.c_double]
+            lib.oracle_delta_steps.restype = ctypes.c_int
+            lib.oracle_delta_steps.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                               dp, dp, dp, dp, dp, dp, dp]
             _lib = lib
     return _lib
 
@@ -316,3 +321,46 @@ def scan_prefix(q, k, v, alpha=None, eps: float = 1e-6, S0=None, z0=None,
         Y[t] = (qf[t] @ S_t) / (den[t] + eps)
     a_T, B_T, b_T = cur[T - 1]
     return Y, a_T * S_in + B_T, a_T * z_in + b_T, den
+
+
+def delta_steps(q, k, v, beta, S0=None):
+    """Delta-rule oracle for one memory: T steps of p = S^T k, e = v - p,
+    S <- S + beta k e^T, y = S^T q (after the write); raw q and k.
+
+    q, k: [T, r]; v: [T, dv]; beta: [T]; S0: [r, dv] (default zero).
+    Returns ``(Y [T, dv], S [r, dv], P [T, dv])`` with P the predictions before each write.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 2 or k.shape != q.shape or v.ndim != 2 or v.shape[0] != q.shape[0] or q.shape[0] == 0:
+        raise ValueError("q, k must be [T, r] of equal shape and v [T, dv] with the same T >= 1")
+    T, r = q.shape
+    dv = v.shape[1]
+    b = _f64(beta).reshape(T)
+    S = np.zeros((r, dv)) if S0 is None else _f64(S0).reshape(r, dv).copy()
+    y = np.empty((T, dv))
+    P = np.empty((T, dv))
+    rc = _load().oracle_delta_steps(T, r, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(S), _ptr(y), _ptr(P))
+    if rc != 0:
+        raise RuntimeError("oracle_delta_steps rejected its arguments")
+    return y, S, P
+
+
+def delta_steps_states(Q, K, V, beta, S0, threads: int = 1):
+    """:func:`delta_steps` over independent memories: Q, K [n, T, r]; V [n, T, dv];
+    beta [n, T]; S0 [n, r, dv].  Returns ``(Y [n, T, dv], S [n, r, dv])``."""
+    Q, K, V, B, S0 = _f64(Q), _f64(K), _f64(V), _f64(beta), _f64(S0)
+    n, T, r = Q.shape
+    dv = V.shape[-1]
+    Y = np.empty((n, T, dv))
+    S = np.empty((n, r, dv))
+
+    def one(h):
+        Y[h], S[h], _ = delta_steps(Q[h], K[h], V[h], B[h], S0[h])
+
+    if threads <= 1 or n == 1:
+        for h in range(n):
+            one(h)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(n)))
+    return Y, S

@@ -46,3 +46,26 @@ def recurrence_exact(qf, kf, v, alpha=None, eps=0):
         nums.append(num)
         dens.append(den)
     return ys, Ss, zs, nums, dens
+
+
+def delta_exact(q, k, v, beta, S0):
+    """The delta rule in rationals: per step p = S^T k, e = v - p, S <- S + beta k e^T,
+    y = S^T q (read after the write).  q, k: T lists of r; v: T lists of dv; beta: T
+    values; S0: r lists of dv.  Returns ``(ys, Ss, preds, errs)`` per step."""
+    S = [[_frac(x) for x in row] for row in S0]
+    r, dv = len(S), len(S[0])
+    ys, Ss, preds, errs = [], [], [], []
+    for t in range(len(k)):
+        k_t = [_frac(x) for x in k[t]]
+        q_t = [_frac(x) for x in q[t]]
+        v_t = [_frac(x) for x in v[t]]
+        b = _frac(beta[t])
+        p = [sum((k_t[i] * S[i][j] for i in range(r)), Fraction(0)) for j in range(dv)]
+        e = [v_t[j] - p[j] for j in range(dv)]
+        S = [[S[i][j] + b * k_t[i] * e[j] for j in range(dv)] for i in range(r)]
+        y = [sum((q_t[i] * S[i][j] for i in range(r)), Fraction(0)) for j in range(dv)]
+        ys.append(y)
+        Ss.append([row[:] for row in S])
+        preds.append(p)
+        errs.append(e)
+    return ys, Ss, preds, errs

@@ -102,3 +102,52 @@ int oracle_recurrence(int64_t T, int32_t r, int32_t dv,
     free(kf);
     return 0;
 }
+
+/*
+ * Delta rule (same page, section "Delta rule：先读旧答案，再写误差", and its
+ * "key 的范数决定了纠错力度" derivation S' = S + beta k (v - k^T S)): a fast-weight
+ * memory without the normaliser of the linear-attention read-out.  Per step t:
+ *   prediction p_t = S^T k_t        (the memory's current answer for key k_t)
+ *   error      e_t = v_t - p_t
+ *   write      S <- S + beta_t k_t e_t^T
+ *   read       y_t = S^T q_t        (after the write, as in the accumulating form)
+ * Keys and queries enter as given: the page's delta examples use raw (unit) keys and
+ * apply no feature map.  The read-out with a query is not printed by the page; reading
+ * it after the write mirrors the update-then-read order of the accumulating form.
+ *
+ * Row-major arrays: q, k [T, r]; v [T, dv]; beta [T]; S [r, dv] in/out; y [T, dv] out;
+ * pred [T, dv] or NULL (out: p_t, the prediction before the write).
+ * Returns 0, or -1 on a bad argument or allocation failure (then nothing is written).
+ */
+int oracle_delta_steps(int64_t T, int32_t r, int32_t dv,
+                       const double *q, const double *k, const double *v, const double *beta,
+                       double *S, double *y, double *pred)
+{
+    if (T < 1 || r < 1 || dv < 1 || !q || !k || !v || !beta || !S || !y)
+        return -1;
+    double *e = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!e)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        const double *kt = k + t * r, *qt = q + t * r;
+        for (int32_t j = 0; j < dv; ++j) {
+            double p = 0.0;
+            for (int32_t i = 0; i < r; ++i)
+                p += kt[i] * S[(int64_t)i * dv + j];
+            if (pred)
+                pred[t * dv + j] = p;
+            e[j] = v[t * dv + j] - p;
+        }
+        for (int32_t i = 0; i < r; ++i)
+            for (int32_t j = 0; j < dv; ++j)
+                S[(int64_t)i * dv + j] = S[(int64_t)i * dv + j] + beta[t] * kt[i] * e[j];
+        for (int32_t j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < r; ++i)
+                acc += qt[i] * S[(int64_t)i * dv + j];
+            y[t * dv + j] = acc;
+        }
+    }
+    free(e);
+    return 0;
+}
