@@ -129,6 +129,26 @@ la_status la_decode_step(const void *q, const void *k, const void *v, const void
                          double eps, void *y, void *S, void *z, la_dtype state_dtype,
                          hipStream_t stream);
 
+/*
+ * la_delta_decode_step -- one delta-rule step for each of n_states independent
+ * memories, updated in place (the fast-weight memory of section "Delta rule：先读旧答案，
+ * 再写误差", written as S' = S + beta k (v - k^T S) under "key 的范数决定了纠错力度"):
+ *   p = S^T k,  e = v - p,  S <- S + beta k e^T,  then y = S^T q.
+ * The memory has no normaliser and q, k enter as given (no feature map): the page's
+ * delta examples use raw keys, and normalised keys keep beta's meaning stable (a step
+ * contracts the error along k by 1 - beta |k|^2).
+ *   q, k   [n_states, d]      io_dtype, read
+ *   v      [n_states, dv]     io_dtype, read
+ *   beta   [n_states]         state_dtype, read (required)
+ *   y      [n_states, dv]     io_dtype, written
+ *   S      [n_states, d, dv]  state_dtype, read and written in place
+ * Same dtype pairs as la_decode_step.  Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE,
+ * LA_ERR_UNSUPPORTED (d or dv > 128), LA_ERR_ALIAS, LA_ERR_LAUNCH.
+ */
+la_status la_delta_decode_step(const void *q, const void *k, const void *v, const void *beta,
+                               la_dtype io_dtype, int64_t n_states, int32_t d, int32_t dv,
+                               void *y, void *S, la_dtype state_dtype, hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char *la_status_str(la_status status);
 

@@ -20,7 +20,7 @@ import threading
 
 __all__ = [
     "LA_F64", "LA_F32", "LA_BF16", "LaArgumentError", "LaLaunchError",
-    "la_state_init", "la_prefill_chunked", "la_decode_step", "la_status_str",
+    "la_state_init", "la_prefill_chunked", "la_decode_step", "la_delta_decode_step", "la_status_str",
     "la_prefill_variant", "library", "library_path",
 ]
 
@@ -79,6 +79,9 @@ def library() -> ctypes.CDLL:
             lib.la_decode_step.restype = ctypes.c_int
             lib.la_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i32, i32, f64, vp, vp, vp,
                                            ctypes.c_int, vp]
+            lib.la_delta_decode_step.restype = ctypes.c_int
+            lib.la_delta_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i32, i32, vp, vp,
+                                                 ctypes.c_int, vp]
             lib.la_prefill_variant.restype = ctypes.c_int32
             lib.la_prefill_variant.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int]
             _lib = lib
@@ -199,6 +202,31 @@ def la_decode_step(q, k, v, alpha, eps: float, y, S, z, stream=None) -> None:
     rc = library().la_decode_step(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, N, d, dv, float(eps),
                                   ptrs[4], ptrs[5], ptrs[6], st, _stream_ptr(q, stream))
     _check(rc, "la_decode_step")
+
+
+def la_delta_decode_step(q, k, v, beta, y, S, stream=None) -> None:
+    """One delta-rule step for N independent memories, S updated in place:
+    e = v - S^T k, S <- S + beta k e^T, y = S^T q (no feature map, no normaliser).
+
+    q, k: [N, d]; v, y: [N, dv]; beta: [N]; S: [N, d, dv].
+    """
+    if q.dim() != 2 or tuple(k.shape) != tuple(q.shape):
+        raise ValueError("q and k must both be [N, d] with the same shape")
+    N, d = q.shape
+    if v.dim() != 2 or v.shape[0] != N:
+        raise ValueError("v must be [N, dv] with q's N")
+    dv = v.shape[1]
+    if tuple(y.shape) != (N, dv) or tuple(S.shape) != (N, d, dv):
+        raise ValueError("y must be [N, dv] and S [N, d, dv]")
+    if beta is None or tuple(beta.shape) != (N,):
+        raise ValueError("beta must be [N]")
+    _same_dtype("q, k, v, y", (q, k, v, y))
+    _same_dtype("S, beta", (S, beta))
+    io, st = _dtype_code(q), _dtype_code(S)
+    ptrs = _device_ptrs(q, k, v, beta, y, S)
+    rc = library().la_delta_decode_step(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, N, d, dv, ptrs[4], ptrs[5], st,
+                                        _stream_ptr(q, stream))
+    _check(rc, "la_delta_decode_step")
 
 
 def la_prefill_variant(io_dtype: int, d: int, dv: int, chunk: int, gated: bool, state_dtype: int) -> int:

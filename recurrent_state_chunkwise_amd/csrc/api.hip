@@ -201,4 +201,29 @@ la_status la_decode_step(const void *q, const void *k, const void *v, const void
     return launched(la::launch_decode(a, io_dtype, stream));
 }
 
+la_status la_delta_decode_step(const void *q, const void *k, const void *v, const void *beta, la_dtype io_dtype,
+                               int64_t n_states, int32_t d, int32_t dv, void *y, void *S, la_dtype state_dtype,
+                               hipStream_t stream)
+{
+    if (!q || !k || !v || !beta || !y || !S)
+        return LA_ERR_NULL;
+    if (n_states < 1 || d < 1 || dv < 1 || n_states > INT32_MAX)
+        return LA_ERR_SHAPE;
+    if (!valid_pair(io_dtype, state_dtype))
+        return LA_ERR_DTYPE;
+    if (d > LA_MAX_WIDTH || dv > LA_MAX_WIDTH)
+        return LA_ERR_UNSUPPORTED;
+    int64_t qk, vy, sb, bb;
+    const int64_t ei = dtype_bytes(io_dtype), es = dtype_bytes(state_dtype);
+    if (!prod_ok({n_states, d, ei}, &qk) || !prod_ok({n_states, dv, ei}, &vy) ||
+        !prod_ok({n_states, d, dv, es}, &sb) || !prod_ok({n_states, es}, &bb))
+        return LA_ERR_SHAPE;
+    if (any_alias({{y, vy}, {S, sb}}, {{q, qk}, {k, qk}, {v, vy}, {beta, bb}}))
+        return LA_ERR_ALIAS;
+
+    la::DeltaArgs a{q, k, v, beta, n_states, d, dv, y, S};
+    (void)hipGetLastError();
+    return launched(la::launch_delta_decode(a, io_dtype, stream));
+}
+
 }  // extern "C"

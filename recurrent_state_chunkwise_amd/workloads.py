@@ -72,6 +72,11 @@ PREFILL_LONG = PrefillConfig(
     "prefill_long_gated_b1_h32_t131072", B=1, H=32, T=131072, d=128, dv=128, io="bf16", chunk=128,
     eps=1e-6, gated=True, gate_mean=4.0, spike_frac=0.1, spike_scale=4.0, seed=5)
 
+# delta-rule decode on the decode workload's memory shape: 65,536 memories of 128 x 128
+DELTA_DECODE = DecodeConfig(
+    "delta_decode_65536_states", requests=128, slots=32, heads=16, d=128, dv=128, seed_writes=0, steps=256,
+    eps=0.0, seed=6, note="unit-norm keys, beta = sigmoid(N(0,1)), memories drawn N(0,1)*0.05")
+
 CONFIGS = {c.name: c for c in (SINGLE_HEAD_F64, PREFILL_UNGATED, PREFILL_GATED, DECODE, PREFILL_LONG)}
 
 
@@ -175,6 +180,32 @@ def decode_step_inputs(cfg: DecodeConfig, step: int, device, n_states=None):
     k = normal((n, cfg.d), cfg.scale, "bf16", gen, device)
     v = normal((n, cfg.dv), cfg.scale, "bf16", gen, device)
     return q, k, v
+
+
+def delta_seed_state(cfg: DecodeConfig, device, n_states=None):
+    """Initial delta-rule memories: [n_states, d, dv] float32, N(0,1) * 0.05."""
+    torch = _torch()
+    n = cfg.n_states if n_states is None else n_states
+    gen = generator(cfg.seed, device)
+    return torch.randn((n, cfg.d, cfg.dv), generator=gen, device=device, dtype=torch.float32).mul_(0.05)
+
+
+def delta_step_inputs(cfg: DecodeConfig, step: int, device, n_states=None):
+    """q, k, v (bf16) and beta (float32) for one delta-rule step, seeded by (seed, step).
+
+    Keys are normalised to unit length in float32 before rounding (the page notes that
+    normalised keys keep beta's meaning stable); beta = sigmoid(N(0,1)) lies in (0, 1),
+    so every step contracts the error along its key.
+    """
+    torch = _torch()
+    n = cfg.n_states if n_states is None else n_states
+    gen = generator(cfg.seed * 1_000_003 + 7919 * (step + 1), device)
+    q = normal((n, cfg.d), cfg.scale, "bf16", gen, device)
+    k = torch.randn((n, cfg.d), generator=gen, device=device, dtype=torch.float32)
+    k = (k / k.norm(dim=1, keepdim=True)).to(torch.bfloat16)
+    v = normal((n, cfg.dv), cfg.scale, "bf16", gen, device)
+    beta = torch.sigmoid(torch.randn((n,), generator=gen, device=device, dtype=torch.float32))
+    return q, k, v, beta
 
 
 def sampled_states(cfg: DecodeConfig, count: int, seed: int = 12345):

@@ -33,8 +33,8 @@ def _declared_functions():
 
 def test_header_symbols_exported(lib):
     names = _declared_functions()
-    assert set(names) >= {"la_state_init", "la_prefill_chunked", "la_decode_step", "la_status_str",
-                          "la_prefill_variant"}
+    assert set(names) >= {"la_state_init", "la_prefill_chunked", "la_decode_step", "la_delta_decode_step",
+                          "la_status_str", "la_prefill_variant"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -103,6 +103,25 @@ def test_decode_rejections(lib):
     assert decode(lib, alpha=P[3]) == ALIAS
 
 
+def delta(lib, q=P[0], k=P[1], v=P[2], beta=P[6], io=BF16, N=4, d=4, dv=4, y=P[3], S=P[4], st=F32):
+    return lib.la_delta_decode_step(q, k, v, beta, io, N, d, dv, y, S, st, None)
+
+
+def test_delta_decode_rejections(lib):
+    assert delta(lib, q=None) == NULL
+    assert delta(lib, beta=None) == NULL          # beta is required
+    assert delta(lib, S=None) == NULL
+    assert delta(lib, N=0) == SHAPE
+    assert delta(lib, N=1 << 33) == SHAPE
+    assert delta(lib, dv=0) == SHAPE
+    assert delta(lib, io=BF16, st=F64) == DTYPE
+    assert delta(lib, io=F64, st=F32) == DTYPE
+    assert delta(lib, d=129) == UNSUP
+    assert delta(lib, y=P[1]) == ALIAS
+    assert delta(lib, S=P[3]) == ALIAS
+    assert delta(lib, beta=P[4]) == ALIAS
+
+
 def test_state_init_rejections(lib):
     assert lib.la_state_init(None, P[1], 1, 4, 4, F32, None) == NULL
     assert lib.la_state_init(P[0], P[1], 0, 4, 4, F32, None) == SHAPE
@@ -138,3 +157,6 @@ def test_binding_shape_contract_cpu():
     with pytest.raises(ValueError):
         la.la_decode_step(torch.zeros(2, 3), torch.zeros(2, 4), torch.zeros(2, 1), None, 1e-6,
                           torch.zeros(2, 1), torch.zeros(2, 3, 1), torch.zeros(2, 3))
+    with pytest.raises(ValueError):
+        la.la_delta_decode_step(torch.zeros(2, 3), torch.zeros(2, 3), torch.zeros(2, 1), None,
+                                torch.zeros(2, 1), torch.zeros(2, 3, 1))
