@@ -41,6 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
 KERNEL_SOURCES = {
     "prefill": ["prefill_mfma.hip", "kernels_general.hip"],
     "decode": ["kernels_general.hip"],
+    "delta": ["delta_decode.hip"],
 }
 
 
@@ -152,6 +153,37 @@ def time_decode(torch, la, wl, cfg, warmup=10, steps=None):
     return total_ms, call_ms
 
 
+DELTA_STATE_STEP_BYTES = 2 * 128 * 128 * 4 + 4 * 256 + 4  # S read and written, q k v y bf16, beta
+
+
+def time_delta(torch, la, wl, cfg, warmup=10, steps=None):
+    """Delta-rule decode: `steps` sequential steps over all memories, inputs pre-generated."""
+    N = cfg.n_states
+    S = wl.delta_seed_state(cfg, "cuda")
+    steps = cfg.steps if steps is None else steps
+    inputs = [wl.delta_step_inputs(cfg, i, "cuda") for i in range(max(steps, warmup))]
+    y = torch.empty((N, cfg.dv), device="cuda", dtype=torch.bfloat16)
+    for i in range(warmup):
+        q, k, v, b = inputs[i]
+        la.la_delta_decode_step(q, k, v, b, y, S)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        q, k, v, b = inputs[i]
+        ev[i][0].record()
+        la.la_delta_decode_step(q, k, v, b, y, S)
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    del inputs, S, y
+    return total_ms, call_ms
+
+
 def cpu_baseline(wl, torch):
     """The FP64 oracle on this host's cores, on a sample of the prefill workload."""
     import oracle
@@ -183,10 +215,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the decode and gated workloads")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "delta", "copy"], default=None,
                     help="run one workload only and print its timing (for profiler runs)")
     ap.add_argument("--decode-steps", type=int, default=None,
-                    help="decode steps to time with --only decode (default: the workload's 1024)")
+                    help="steps to time with --only decode or --only delta (default: the workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -213,6 +245,11 @@ def main():
         steps = args.decode_steps or wl.DECODE.steps
         d_total, d_call = time_decode(torch, la, wl, wl.DECODE, steps=steps)
         print(json.dumps({"only": "decode", "steps": steps, "ms_per_step": d_total / steps, "call_ms": d_call}))
+        return
+    if args.only == "delta":
+        steps = args.decode_steps or wl.DELTA_DECODE.steps
+        d_total, d_call = time_delta(torch, la, wl, wl.DELTA_DECODE, steps=steps)
+        print(json.dumps({"only": "delta", "steps": steps, "ms_per_step": d_total / steps, "call_ms": d_call}))
         return
     cfg = wl.PREFILL_UNGATED
     torch.cuda.synchronize()
@@ -274,6 +311,19 @@ def main():
                          "frac": d_bytes / (d_call / 1e3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": measured_traffic("decode"),
                          "call_ms": d_call, "algorithmic_bytes": d_bytes},
+        }
+        xcfg = wl.DELTA_DECODE
+        x_total, x_call = time_delta(torch, la, wl, xcfg)
+        x_bytes = xcfg.n_states * DELTA_STATE_STEP_BYTES
+        out["delta_decode"] = {
+            "workload": xcfg.name, "steps": xcfg.steps,
+            "value": xcfg.n_states * xcfg.steps / (x_total / 1e3), "unit": "state-steps/s",
+            "ms_per_step": x_total / xcfg.steps,
+            "roofline": {"kernel": "la_delta_decode_step", "bound": "hbm",
+                         "achieved": x_bytes / (x_call / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": x_bytes / (x_call / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("delta"),
+                         "call_ms": x_call, "algorithmic_bytes": x_bytes},
         }
         other = []
         for ocfg in (wl.PREFILL_GATED, wl.PREFILL_LONG):
