@@ -26,6 +26,16 @@ Source of truth is the page "Linear attention：把历史写进状态"
   tree order.
 * :func:`delta_steps` -- the delta rule of section "Delta rule：先读旧答案，再写误差"
   (S <- S + beta k (v - S^T k), read y = S^T q after the write), also in C.
+* :func:`noncausal` -- the non-causal form of the page "线性注意力架构演进"
+  (ai-master.cc): all keys and values are written into the state first, then
+  every query reads the full state (eps added to the denominator), in C;
+  :func:`quadratic_unmasked` is its brute-force unmasked counterpart.
+
+Feature maps (``phi_mode``): ``"elu1"`` (ELU+1, the default), ``"relu1"``
+(max(x,0)+1, the positive map of the datawhalechina chapter "Linear Attention and
+Recurrent State"), ``"relu_eps"`` and ``"sigmoid_eps"`` (max(x,0)+1e-5 and
+sigmoid(x)+1e-5, the switchable maps of the ai-master.cc page's pluggable module)
+and ``"identity"`` (the inputs already are features, for worked examples).
 
 Every function here is pinned by the CPU tests against the page's worked
 examples, closed forms and brute force (see ``tests/test_oracle_pins.py``).
@@ -46,7 +56,12 @@ _LIB_PATH = os.path.join(_HERE, "liblinattn_oracle.so")
 
 PHI_ELU1 = 0
 PHI_IDENTITY = 1
-_PHI_MODES = {"elu1": PHI_ELU1, "identity": PHI_IDENTITY}
+PHI_RELU1 = 2
+PHI_RELU_EPS = 3
+PHI_SIGMOID_EPS = 4
+_PHI_MODES = {"elu1": PHI_ELU1, "identity": PHI_IDENTITY, "relu1": PHI_RELU1,
+              "relu_eps": PHI_RELU_EPS, "sigmoid_eps": PHI_SIGMOID_EPS}
+PHI_MODES = tuple(_PHI_MODES)
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -81,6 +96,12 @@ def _load():
                                               dp, dp, dp, dp]
             lib.oracle_phi.restype = ctypes.c_double
             lib.oracle_phi.argtypes = [ctypes.c_double]
+            lib.oracle_phi_mode.restype = ctypes.c_double
+            lib.oracle_phi_mode.argtypes = [ctypes.c_double, ctypes.c_int32]
+            lib.oracle_noncausal.restype = ctypes.c_int
+            lib.oracle_noncausal.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             dp, dp, dp, ctypes.c_double, ctypes.c_int32,
+                                             dp, dp, dp, dp]
             lib.oracle_delta_steps.restype = ctypes.c_int
             lib.oracle_delta_steps.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                dp, dp, dp, dp, dp, dp, dp]
@@ -104,17 +125,39 @@ def phi(x) -> np.ndarray:
     return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def phi_scalar_c(x: float) -> float:
+def phi_scalar_c(x: float, phi_mode: str = "elu1") -> float:
     """The C oracle's own feature map, for pinning it to the closed form."""
-    return _load().oracle_phi(float(x))
+    if phi_mode == "elu1":
+        return _load().oracle_phi(float(x))
+    return _load().oracle_phi_mode(float(x), _mode_code(phi_mode))
+
+
+def _mode_code(phi_mode: str) -> int:
+    if phi_mode not in _PHI_MODES:
+        raise ValueError("phi_mode must be one of %s" % ", ".join(PHI_MODES))
+    return _PHI_MODES[phi_mode]
 
 
 def _features(x: np.ndarray, phi_mode: str) -> np.ndarray:
+    """The feature maps in NumPy (used by the matrix forms; the C oracle has its own)."""
+    x = np.asarray(x, dtype=np.float64)
     if phi_mode == "identity":
-        return np.asarray(x, dtype=np.float64)
+        return x
     if phi_mode == "elu1":
         return phi(x)
-    raise ValueError("phi_mode must be 'elu1' or 'identity'")
+    if phi_mode == "relu1":
+        return np.maximum(x, 0.0) + 1.0
+    if phi_mode == "relu_eps":
+        return np.maximum(x, 0.0) + 1e-5
+    if phi_mode == "sigmoid_eps":
+        with np.errstate(over="ignore"):
+            return 1.0 / (1.0 + np.exp(-x)) + 1e-5
+    raise ValueError("phi_mode must be one of %s" % ", ".join(PHI_MODES))
+
+
+def features(x, phi_mode: str = "elu1") -> np.ndarray:
+    """phi applied elementwise, for any of the modes."""
+    return _features(x, phi_mode)
 
 
 def recurrence(q, k, v, alpha=None, eps: float = 1e-6, S0=None, z0=None,
@@ -137,10 +180,8 @@ def recurrence(q, k, v, alpha=None, eps: float = 1e-6, S0=None, z0=None,
     z = np.zeros(r) if z0 is None else _f64(z0).reshape(r).copy()
     y = np.empty((T, dv))
     den = np.empty(T)
-    if phi_mode not in _PHI_MODES:
-        raise ValueError("phi_mode must be 'elu1' or 'identity'")
     rc = _load().oracle_recurrence(T, r, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(a), float(eps),
-                                   _PHI_MODES[phi_mode], _ptr(S), _ptr(z), _ptr(y), _ptr(den))
+                                   _mode_code(phi_mode), _ptr(S), _ptr(z), _ptr(y), _ptr(den))
     if rc != 0:
         raise RuntimeError("oracle_recurrence rejected its arguments")
     return y, S, z, den
@@ -364,3 +405,72 @@ def delta_steps_states(Q, K, V, beta, S0, threads: int = 1):
         with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(one, range(n)))
     return Y, S
+
+
+def noncausal(q, k, v, eps: float = 1e-6, S0=None, z0=None, phi_mode: str = "elu1"):
+    """Non-causal oracle for one sequence: S = S0 + sum_t k~_t v_t^T, z = z0 + sum_t k~_t
+    over the whole sequence, then y_t = q~_t^T S / (q~_t^T z + eps) for every t.
+
+    Shapes as :func:`recurrence`.  Returns ``(Y [T, dv], S [r, dv], z [r], den [T])``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 2 or k.shape != q.shape or v.ndim != 2 or v.shape[0] != q.shape[0] or q.shape[0] == 0:
+        raise ValueError("q, k must be [T, r] of equal shape and v [T, dv] with the same T >= 1")
+    T, r = q.shape
+    dv = v.shape[1]
+    if r == 0 or dv == 0:
+        raise ValueError("feature and value widths must be >= 1")
+    S = np.zeros((r, dv)) if S0 is None else _f64(S0).reshape(r, dv).copy()
+    z = np.zeros(r) if z0 is None else _f64(z0).reshape(r).copy()
+    y = np.empty((T, dv))
+    den = np.empty(T)
+    rc = _load().oracle_noncausal(T, r, dv, _ptr(q), _ptr(k), _ptr(v), float(eps), _mode_code(phi_mode),
+                                  _ptr(S), _ptr(z), _ptr(y), _ptr(den))
+    if rc != 0:
+        raise RuntimeError("oracle_noncausal rejected its arguments")
+    return y, S, z, den
+
+
+def noncausal_heads(Q, K, V, eps: float = 1e-6, S0=None, z0=None, phi_mode: str = "elu1",
+                    threads: int = 1):
+    """:func:`noncausal` over independent heads (shapes as :func:`recurrence_heads`)."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    lead = Q.shape[:-2]
+    T, r = Q.shape[-2:]
+    dv = V.shape[-1]
+    n = int(np.prod(lead)) if lead else 1
+    Qf, Kf, Vf = Q.reshape(n, T, r), K.reshape(n, T, r), V.reshape(n, T, dv)
+    Sf = None if S0 is None else _f64(S0).reshape(n, r, dv)
+    zf = None if z0 is None else _f64(z0).reshape(n, r)
+    Y = np.empty((n, T, dv))
+    S = np.empty((n, r, dv))
+    z = np.empty((n, r))
+    den = np.empty((n, T))
+
+    def one(h):
+        Y[h], S[h], z[h], den[h] = noncausal(Qf[h], Kf[h], Vf[h], eps, None if Sf is None else Sf[h],
+                                             None if zf is None else zf[h], phi_mode)
+
+    if threads <= 1 or n == 1:
+        for h in range(n):
+            one(h)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(n)))
+    return (Y.reshape(*lead, T, dv), S.reshape(*lead, r, dv), z.reshape(*lead, r),
+            den.reshape(*lead, T))
+
+
+def quadratic_unmasked(q, k, v, eps: float = 1e-6, S0=None, z0=None, phi_mode: str = "elu1"):
+    """Brute-force unmasked form: A = Q~ K~^T over all pairs (no causal mask),
+    Y = (Q~ S0 + A V) / (Q~ z0 + rowsum(A) + eps).  Returns ``(Y, den)``."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    qf, kf = _features(q, phi_mode), _features(k, phi_mode)
+    A = qf @ kf.T
+    num = A @ v
+    den = A.sum(axis=1)
+    if S0 is not None:
+        num = num + qf @ _f64(S0)
+    if z0 is not None:
+        den = den + qf @ _f64(z0)
+    return num / (den + eps)[:, None], den

@@ -28,17 +28,51 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#define ORACLE_PHI_ELU1 0     /* phi(x) = ELU(x) + 1 */
-#define ORACLE_PHI_IDENTITY 1 /* the inputs already are features (worked examples) */
+#define ORACLE_PHI_ELU1 0        /* phi(x) = ELU(x) + 1 */
+#define ORACLE_PHI_IDENTITY 1    /* the inputs already are features (worked examples) */
+#define ORACLE_PHI_RELU1 2       /* phi(x) = max(x, 0) + 1 */
+#define ORACLE_PHI_RELU_EPS 3    /* phi(x) = max(x, 0) + 1e-5 */
+#define ORACLE_PHI_SIGMOID_EPS 4 /* phi(x) = 1 / (1 + exp(-x)) + 1e-5 */
 
 double oracle_phi(double x)
 {
     return x > 0.0 ? x + 1.0 : exp(x);
 }
 
+/*
+ * The other positive feature maps the pages use:
+ *   - max(x, 0) + 1: the teaching map of the datawhalechina chapter "Linear Attention and
+ *     Recurrent State" (Step 4, its positive feature map: positive by construction, so
+ *     the normaliser never vanishes);
+ *   - max(x, 0) + 1e-5 and sigmoid(x) + 1e-5: the selectable maps of the pluggable
+ *     linear-attention module of the page "线性注意力架构演进：从 Transformer 瓶颈到高效
+ *     推理" (ai-master.cc, its third replacement plan, whose feature-map switch offers
+ *     elu, relu and sigmoid).
+ */
+double oracle_phi_mode(double x, int32_t phi_mode)
+{
+    switch (phi_mode) {
+    case ORACLE_PHI_IDENTITY:
+        return x;
+    case ORACLE_PHI_RELU1:
+        return (x > 0.0 ? x : 0.0) + 1.0;
+    case ORACLE_PHI_RELU_EPS:
+        return (x > 0.0 ? x : 0.0) + 1e-5;
+    case ORACLE_PHI_SIGMOID_EPS:
+        return 1.0 / (1.0 + exp(-x)) + 1e-5;
+    default:
+        return oracle_phi(x);
+    }
+}
+
+static int known_phi_mode(int32_t phi_mode)
+{
+    return phi_mode >= ORACLE_PHI_ELU1 && phi_mode <= ORACLE_PHI_SIGMOID_EPS;
+}
+
 static double apply_feature_map(double x, int32_t phi_mode)
 {
-    return phi_mode == ORACLE_PHI_IDENTITY ? x : oracle_phi(x);
+    return oracle_phi_mode(x, phi_mode);
 }
 
 /*
@@ -59,7 +93,7 @@ int oracle_recurrence(int64_t T, int32_t r, int32_t dv,
 {
     if (T < 1 || r < 1 || dv < 1 || !q || !k || !v || !S || !z || !y)
         return -1;
-    if (phi_mode != ORACLE_PHI_ELU1 && phi_mode != ORACLE_PHI_IDENTITY)
+    if (!known_phi_mode(phi_mode))
         return -1;
 
     double *qf = (double *)malloc(sizeof(double) * (size_t)r);
@@ -100,6 +134,61 @@ int oracle_recurrence(int64_t T, int32_t r, int32_t dv,
 
     free(qf);
     free(kf);
+    return 0;
+}
+
+/*
+ * Non-causal form: every query reads the state that holds the whole sequence.  This is
+ * the associative-order evaluation of the page "线性注意力架构演进" (ai-master.cc): its
+ * LinearAttention class's parallel training form and its pluggable module both form
+ * K~^T V and the key sum once and read each query against them.  With S0 = z0 = 0 it
+ * equals unmasked attention with weights phi(q_t).phi(k_i).  The epsilon convention is
+ * the one of the read-out above: eps is added to the denominator.
+ *   S <- S0 + sum_t phi(k_t) v_t^T,   z <- z0 + sum_t phi(k_t)     (t = 0 .. T-1)
+ *   y_t = (phi(q_t)^T S) / (phi(q_t)^T z + eps)                      for every t
+ * Arrays as for oracle_recurrence; S and z are in/out (in: the state before the
+ * sequence, out: the state after it).  den [T] or NULL receives phi(q_t)^T z.
+ */
+int oracle_noncausal(int64_t T, int32_t r, int32_t dv,
+                     const double *q, const double *k, const double *v,
+                     double eps, int32_t phi_mode,
+                     double *S, double *z, double *y, double *den)
+{
+    if (T < 1 || r < 1 || dv < 1 || !q || !k || !v || !S || !z || !y)
+        return -1;
+    if (!known_phi_mode(phi_mode))
+        return -1;
+    double *qf = (double *)malloc(sizeof(double) * (size_t)r);
+    if (!qf)
+        return -1;
+
+    /* write every token into the state */
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t i = 0; i < r; ++i) {
+            const double kf = apply_feature_map(k[t * r + i], phi_mode);
+            for (int32_t j = 0; j < dv; ++j)
+                S[(int64_t)i * dv + j] = S[(int64_t)i * dv + j] + kf * v[t * dv + j];
+            z[i] = z[i] + kf;
+        }
+    }
+
+    /* read every query against the full state */
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t i = 0; i < r; ++i)
+            qf[i] = apply_feature_map(q[t * r + i], phi_mode);
+        double d = 0.0;
+        for (int32_t i = 0; i < r; ++i)
+            d += qf[i] * z[i];
+        if (den)
+            den[t] = d;
+        for (int32_t j = 0; j < dv; ++j) {
+            double num = 0.0;
+            for (int32_t i = 0; i < r; ++i)
+                num += qf[i] * S[(int64_t)i * dv + j];
+            y[t * dv + j] = num / (d + eps);
+        }
+    }
+    free(qf);
     return 0;
 }
 
