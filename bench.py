@@ -12,11 +12,13 @@ line also carries:
   decode        the batched decode workload (65,536 fp32 states seeded by 256
                 writes, 1,024 sequential steps) in state-steps/s with its HBM roofline
                 (133,120 B per state-step);
+  noncausal     la_prefill_noncausal on the ungated prefill shape (every query reads
+                the state of the whole sequence), timed the same way, same roofline bytes;
   other         the gated prefill workloads, timed the same way;
   cpu_baseline  the FP64 oracle timed on this host's cores on a sample of the
                 prefill workload.
 Run: python bench.py [--gpus 1] [--steps K] [--warmup W]
-     python bench.py --only prefill|decode|copy   (one workload, for profiler runs; `copy`
+     python bench.py --only prefill|noncausal|decode|delta|copy   (one workload, for profiler runs; `copy`
      is a plain 1 GiB device-to-device copy used to calibrate the HBM byte counters)
 """
 from __future__ import annotations
@@ -42,6 +44,7 @@ KERNEL_SOURCES = {
     "prefill": ["prefill_mfma.hip", "kernels_general.hip"],
     "decode": ["kernels_general.hip"],
     "delta": ["delta_decode.hip"],
+    "noncausal": ["prefill_mfma.hip", "kernels_general.hip"],
 }
 
 
@@ -79,10 +82,10 @@ def prefill_useful_flops(B, H, T, C, d=128, dv=128):
     return B * H * T * ((C + 1) * (d + dv) + 4 * d * dv)
 
 
-def time_prefill(torch, la, wl, cfg, steps, warmup, sets=2):
-    """Time la_prefill_chunked; step i uses input set i % sets.  Two sets of the ungated
-    workload (2 x 201 MB of Q, K, V) exceed the 256 MB last-level cache, so a timed call
-    cannot find its inputs left in it by the previous call."""
+def time_prefill(torch, la, wl, cfg, steps, warmup, sets=2, noncausal=False):
+    """Time la_prefill_chunked (or la_prefill_noncausal); step i uses input set i % sets.
+    Two sets of the ungated workload (2 x 201 MB of Q, K, V) exceed the 256 MB last-level
+    cache, so a timed call cannot find its inputs left in it by the previous call."""
     inputs = [wl.prefill_inputs(cfg, "cuda", seed=cfg.seed + 1000 * i) for i in range(sets)]
     Y = torch.empty_like(inputs[0][2])
     S = torch.empty((cfg.B, cfg.H, cfg.d, cfg.dv), device="cuda")
@@ -90,7 +93,10 @@ def time_prefill(torch, la, wl, cfg, steps, warmup, sets=2):
 
     def call(i):
         Q, K, V, A = inputs[i % sets]
-        la.la_prefill_chunked(Q, K, V, A, cfg.eps, cfg.chunk, Y, S, z)
+        if noncausal:
+            la.la_prefill_noncausal(Q, K, V, cfg.eps, Y, S, z)
+        else:
+            la.la_prefill_chunked(Q, K, V, A, cfg.eps, cfg.chunk, Y, S, z)
 
     for i in range(warmup):
         la.la_state_init(S, z)
@@ -215,7 +221,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the decode and gated workloads")
-    ap.add_argument("--only", choices=["prefill", "decode", "delta", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "noncausal", "decode", "delta", "copy"], default=None,
                     help="run one workload only and print its timing (for profiler runs)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="steps to time with --only decode or --only delta (default: the workload's)")
@@ -252,6 +258,11 @@ def main():
         print(json.dumps({"only": "delta", "steps": steps, "ms_per_step": d_total / steps, "call_ms": d_call}))
         return
     cfg = wl.PREFILL_UNGATED
+    if args.only == "noncausal":
+        n_total, n_call, _ = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, noncausal=True)
+        print(json.dumps({"only": "noncausal", "steps": args.steps, "ms_per_step": n_total / args.steps,
+                          "call_ms": n_call}))
+        return
     torch.cuda.synchronize()
     total_ms, call_ms, wall = time_prefill(torch, la, wl, cfg, args.steps, args.warmup)
     # the same call on one input set, whose inputs may stay in the last-level cache (reported only)
@@ -324,6 +335,15 @@ def main():
                          "frac": x_bytes / (x_call / 1e3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": measured_traffic("delta"),
                          "call_ms": x_call, "algorithmic_bytes": x_bytes},
+        }
+        n_total, n_call, _ = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, noncausal=True)
+        out["noncausal"] = {
+            "workload": "noncausal_" + cfg.name, "value": tokens / (n_call / 1e3), "unit": "tokens/s",
+            "roofline": {"kernel": "la_prefill_noncausal (segment sums + read-out)", "bound": "hbm",
+                         "achieved": nbytes / (n_call / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": nbytes / (n_call / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("noncausal"),
+                         "call_ms": n_call, "algorithmic_bytes": nbytes},
         }
         other = []
         for ocfg in (wl.PREFILL_GATED, wl.PREFILL_LONG):

@@ -54,7 +54,8 @@ typedef enum la_status {
     LA_ERR_CHUNK = 5,       /* chunk < 1 */
     LA_ERR_UNSUPPORTED = 6, /* valid request with no kernel: d or dv > 128, chunk > 128 */
     LA_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
-    LA_ERR_ALIAS = 8        /* an output overlaps an input or another output */
+    LA_ERR_ALIAS = 8,       /* an output overlaps an input or another output */
+    LA_ERR_PHI = 9          /* unknown feature map */
 } la_status;
 
 typedef enum la_dtype {
@@ -62,6 +63,24 @@ typedef enum la_dtype {
     LA_F32 = 1,
     LA_BF16 = 2
 } la_dtype;
+
+/*
+ * Feature maps phi, applied elementwise to queries and keys.  Every entry point without
+ * an la_feature_map argument uses LA_PHI_ELU1.
+ *   LA_PHI_ELU1         ELU(x) + 1 = x + 1 (x > 0), exp(x) (x <= 0)     (hs-black.github.io
+ *                       page, section "关键改写：让求和先发生")
+ *   LA_PHI_RELU1        max(x, 0) + 1       (datawhalechina chapter "Linear Attention and
+ *                       Recurrent State", Step 4: its positive feature map)
+ *   LA_PHI_RELU_EPS     max(x, 0) + 1e-5    (page "线性注意力架构演进", ai-master.cc: the
+ *   LA_PHI_SIGMOID_EPS  sigmoid(x) + 1e-5    feature-map switch of its pluggable module)
+ * All four are strictly positive for finite x, so the denominator stays positive.
+ */
+typedef enum la_feature_map {
+    LA_PHI_ELU1 = 0,
+    LA_PHI_RELU1 = 1,
+    LA_PHI_RELU_EPS = 2,
+    LA_PHI_SIGMOID_EPS = 3
+} la_feature_map;
 
 /* Largest feature width d (= r), value width dv and chunk any kernel handles. */
 #define LA_MAX_WIDTH 128
@@ -148,6 +167,49 @@ la_status la_decode_step(const void *q, const void *k, const void *v, const void
 la_status la_delta_decode_step(const void *q, const void *k, const void *v, const void *beta,
                                la_dtype io_dtype, int64_t n_states, int32_t d, int32_t dv,
                                void *y, void *S, la_dtype state_dtype, hipStream_t stream);
+
+/*
+ * la_prefill_chunked_fm, la_decode_step_fm -- la_prefill_chunked and la_decode_step with
+ * the feature map chosen by `phi` (same arguments, then `phi` before the stream).
+ * An unknown `phi` is LA_ERR_PHI; everything else is as for the call without _fm.
+ */
+la_status la_prefill_chunked_fm(const void *Q, const void *K, const void *V, const void *alpha,
+                                la_dtype io_dtype, int64_t B, int64_t H, int64_t T,
+                                int32_t d, int32_t dv, double eps, int32_t chunk,
+                                void *Y, void *S, void *z, la_dtype state_dtype,
+                                la_feature_map phi, hipStream_t stream);
+
+la_status la_decode_step_fm(const void *q, const void *k, const void *v, const void *alpha,
+                            la_dtype io_dtype, int64_t n_states, int32_t d, int32_t dv,
+                            double eps, void *y, void *S, void *z, la_dtype state_dtype,
+                            la_feature_map phi, hipStream_t stream);
+
+/*
+ * la_prefill_noncausal -- the non-causal form: every token of a sequence is written into
+ * the state first, then every query reads that full state (page "线性注意力架构演进",
+ * ai-master.cc: its linear-attention module's parallel form and its pluggable module
+ * form K~^T V and the key sum once and read each query against them; eps is added to
+ * the denominator as in the causal read-out):
+ *   S_out = S_in + sum_t k~_t v_t^T,   z_out = z_in + sum_t k~_t
+ *   y_t   = (q~_t^T S_out) / (q~_t^T z_out + eps)        for every t
+ * With S_in = z_in = 0 (la_state_init) this is unmasked attention with weights
+ * q~_t . k~_i; a nonzero incoming state is context that every query also sees.  There
+ * is no gate: a decay has no direction in this form.
+ *   Q, K   [B, H, T, d]   io_dtype, read
+ *   V      [B, H, T, dv]  io_dtype, read
+ *   Y      [B, H, T, dv]  io_dtype, written
+ *   S      [B, H, d, dv]  state_dtype, read (S_in) and overwritten with S_out
+ *   z      [B, H, d]      state_dtype, same as S
+ * bf16 io with d = dv = 128 runs on bf16 MFMA (fp32 accumulation, the state rounded
+ * to bf16 for the read as in the causal inter-chunk read); other valid requests run a
+ * general kernel in the state dtype.
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_EPS, LA_ERR_UNSUPPORTED
+ * (d or dv > 128), LA_ERR_ALIAS, LA_ERR_PHI, LA_ERR_LAUNCH.
+ */
+la_status la_prefill_noncausal(const void *Q, const void *K, const void *V, la_dtype io_dtype,
+                               int64_t B, int64_t H, int64_t T, int32_t d, int32_t dv,
+                               double eps, void *Y, void *S, void *z, la_dtype state_dtype,
+                               la_feature_map phi, hipStream_t stream);
 
 /* Static description of a status code; never NULL. */
 const char *la_status_str(la_status status);

@@ -19,16 +19,21 @@ import os
 import threading
 
 __all__ = [
-    "LA_F64", "LA_F32", "LA_BF16", "LaArgumentError", "LaLaunchError",
-    "la_state_init", "la_prefill_chunked", "la_decode_step", "la_delta_decode_step", "la_status_str",
-    "la_prefill_variant", "library", "library_path",
+    "LA_F64", "LA_F32", "LA_BF16", "LA_PHI_ELU1", "LA_PHI_RELU1", "LA_PHI_RELU_EPS", "LA_PHI_SIGMOID_EPS",
+    "FEATURE_MAPS", "LaArgumentError", "LaLaunchError",
+    "la_state_init", "la_prefill_chunked", "la_prefill_chunked_fm", "la_prefill_noncausal", "la_decode_step",
+    "la_decode_step_fm", "la_delta_decode_step", "la_status_str", "la_prefill_variant", "library", "library_path",
 ]
 
 LA_F64, LA_F32, LA_BF16 = 0, 1, 2
+LA_PHI_ELU1, LA_PHI_RELU1, LA_PHI_RELU_EPS, LA_PHI_SIGMOID_EPS = 0, 1, 2, 3
+# feature-map names accepted by the *_fm calls and la_prefill_noncausal
+FEATURE_MAPS = {"elu1": LA_PHI_ELU1, "relu1": LA_PHI_RELU1, "relu_eps": LA_PHI_RELU_EPS,
+                "sigmoid_eps": LA_PHI_SIGMOID_EPS}
 
 STATUS = {
     0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE", 4: "LA_ERR_EPS",
-    5: "LA_ERR_CHUNK", 6: "LA_ERR_UNSUPPORTED", 7: "LA_ERR_LAUNCH", 8: "LA_ERR_ALIAS",
+    5: "LA_ERR_CHUNK", 6: "LA_ERR_UNSUPPORTED", 7: "LA_ERR_LAUNCH", 8: "LA_ERR_ALIAS", 9: "LA_ERR_PHI",
 }
 LA_ERR_LAUNCH = 7
 
@@ -82,6 +87,15 @@ def library() -> ctypes.CDLL:
             lib.la_delta_decode_step.restype = ctypes.c_int
             lib.la_delta_decode_step.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i32, i32, vp, vp,
                                                  ctypes.c_int, vp]
+            lib.la_prefill_chunked_fm.restype = ctypes.c_int
+            lib.la_prefill_chunked_fm.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i32, i32, f64, i32,
+                                                  vp, vp, vp, ctypes.c_int, ctypes.c_int, vp]
+            lib.la_decode_step_fm.restype = ctypes.c_int
+            lib.la_decode_step_fm.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i32, i32, f64, vp, vp, vp,
+                                              ctypes.c_int, ctypes.c_int, vp]
+            lib.la_prefill_noncausal.restype = ctypes.c_int
+            lib.la_prefill_noncausal.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i32, i32, f64, vp, vp, vp,
+                                                 ctypes.c_int, ctypes.c_int, vp]
             lib.la_prefill_variant.restype = ctypes.c_int32
             lib.la_prefill_variant.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int]
             _lib = lib
@@ -153,6 +167,61 @@ def la_state_init(S, z, stream=None) -> None:
     _check(library().la_state_init(pS, pz, n, r, dv, st, _stream_ptr(S, stream)), "la_state_init")
 
 
+def _phi_code(phi) -> int:
+    """A feature-map name of FEATURE_MAPS or an la_feature_map code (an unknown code is
+    passed through, for the library to reject)."""
+    if isinstance(phi, str):
+        if phi not in FEATURE_MAPS:
+            raise ValueError("unknown feature map %r (one of %s)" % (phi, ", ".join(FEATURE_MAPS)))
+        return FEATURE_MAPS[phi]
+    return int(phi)
+
+
+def _prefill_shapes(Q, K, V, Y, S, z):
+    if Q.dim() != 4 or tuple(K.shape) != tuple(Q.shape):
+        raise ValueError("Q and K must both be [B, H, T, d] with the same shape")
+    B, H, T, d = Q.shape
+    if V.dim() != 4 or tuple(V.shape[:3]) != (B, H, T):
+        raise ValueError("V must be [B, H, T, dv] with Q's B, H, T")
+    dv = V.shape[3]
+    if tuple(Y.shape) != tuple(V.shape):
+        raise ValueError("Y must have V's shape")
+    if tuple(S.shape) != (B, H, d, dv) or tuple(z.shape) != (B, H, d):
+        raise ValueError("S must be [B, H, d, dv] and z [B, H, d]")
+    return B, H, T, d, dv
+
+
+def la_prefill_chunked_fm(Q, K, V, alpha, eps: float, chunk: int, Y, S, z, phi="elu1", stream=None) -> None:
+    """:func:`la_prefill_chunked` with the feature map ``phi`` (a FEATURE_MAPS name or code)."""
+    B, H, T, d, dv = _prefill_shapes(Q, K, V, Y, S, z)
+    if alpha is not None and tuple(alpha.shape) != (B, H, T):
+        raise ValueError("alpha must be [B, H, T]")
+    _same_dtype("Q, K, V, Y", (Q, K, V, Y))
+    _same_dtype("S, z, alpha", (S, z, alpha))
+    io, st = _dtype_code(Q), _dtype_code(S)
+    ptrs = _device_ptrs(Q, K, V, alpha, Y, S, z)
+    rc = library().la_prefill_chunked_fm(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, B, H, T, d, dv, float(eps),
+                                         int(chunk), ptrs[4], ptrs[5], ptrs[6], st, _phi_code(phi),
+                                         _stream_ptr(Q, stream))
+    _check(rc, "la_prefill_chunked_fm")
+
+
+def la_prefill_noncausal(Q, K, V, eps: float, Y, S, z, phi="elu1", stream=None) -> None:
+    """Non-causal form of B*H sequences: (S, z) += the whole sequence, then every query
+    reads the final state: Y_t = q~_t^T S / (q~_t^T z + eps).
+
+    Q, K: [B, H, T, d]; V, Y: [B, H, T, dv]; S: [B, H, d, dv], z: [B, H, d] in/out.
+    """
+    B, H, T, d, dv = _prefill_shapes(Q, K, V, Y, S, z)
+    _same_dtype("Q, K, V, Y", (Q, K, V, Y))
+    _same_dtype("S, z", (S, z))
+    io, st = _dtype_code(Q), _dtype_code(S)
+    ptrs = _device_ptrs(Q, K, V, Y, S, z)
+    rc = library().la_prefill_noncausal(ptrs[0], ptrs[1], ptrs[2], io, B, H, T, d, dv, float(eps), ptrs[3],
+                                        ptrs[4], ptrs[5], st, _phi_code(phi), _stream_ptr(Q, stream))
+    _check(rc, "la_prefill_noncausal")
+
+
 def la_prefill_chunked(Q, K, V, alpha, eps: float, chunk: int, Y, S, z, stream=None) -> None:
     """Chunked prefill of B*H sequences, continuing from (S, z), writing Y and the final (S, z).
 
@@ -202,6 +271,27 @@ def la_decode_step(q, k, v, alpha, eps: float, y, S, z, stream=None) -> None:
     rc = library().la_decode_step(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, N, d, dv, float(eps),
                                   ptrs[4], ptrs[5], ptrs[6], st, _stream_ptr(q, stream))
     _check(rc, "la_decode_step")
+
+
+def la_decode_step_fm(q, k, v, alpha, eps: float, y, S, z, phi="elu1", stream=None) -> None:
+    """:func:`la_decode_step` with the feature map ``phi`` (a FEATURE_MAPS name or code)."""
+    if q.dim() != 2 or tuple(k.shape) != tuple(q.shape):
+        raise ValueError("q and k must both be [N, d] with the same shape")
+    N, d = q.shape
+    if v.dim() != 2 or v.shape[0] != N:
+        raise ValueError("v must be [N, dv] with q's N")
+    dv = v.shape[1]
+    if tuple(y.shape) != (N, dv) or tuple(S.shape) != (N, d, dv) or tuple(z.shape) != (N, d):
+        raise ValueError("y must be [N, dv], S [N, d, dv] and z [N, d]")
+    if alpha is not None and tuple(alpha.shape) != (N,):
+        raise ValueError("alpha must be [N]")
+    _same_dtype("q, k, v, y", (q, k, v, y))
+    _same_dtype("S, z, alpha", (S, z, alpha))
+    io, st = _dtype_code(q), _dtype_code(S)
+    ptrs = _device_ptrs(q, k, v, alpha, y, S, z)
+    rc = library().la_decode_step_fm(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, N, d, dv, float(eps),
+                                     ptrs[4], ptrs[5], ptrs[6], st, _phi_code(phi), _stream_ptr(q, stream))
+    _check(rc, "la_decode_step_fm")
 
 
 def la_delta_decode_step(q, k, v, beta, y, S, stream=None) -> None:

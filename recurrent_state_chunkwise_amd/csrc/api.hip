@@ -70,6 +70,11 @@ bool any_alias(std::initializer_list<Range> outs, std::initializer_list<Range> i
 
 bool eps_ok(double eps) { return isfinite(eps) && eps >= 0.0; }
 
+bool phi_ok(la_feature_map phi)
+{
+    return phi == LA_PHI_ELU1 || phi == LA_PHI_RELU1 || phi == LA_PHI_RELU_EPS || phi == LA_PHI_SIGMOID_EPS;
+}
+
 la_status launched(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }
 
 // Scalar checks shared by la_prefill_chunked and la_prefill_variant.
@@ -111,6 +116,8 @@ const char *la_status_str(la_status s)
         return "the HIP runtime refused a kernel launch";
     case LA_ERR_ALIAS:
         return "an output buffer overlaps an input or another output";
+    case LA_ERR_PHI:
+        return "unknown feature map";
     }
     return "unknown status";
 }
@@ -143,9 +150,10 @@ int32_t la_prefill_variant(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chu
     return la::mfma_prefill_supported(io_dtype, d, dv, chunk) ? 1 : 0;
 }
 
-la_status la_prefill_chunked(const void *Q, const void *K, const void *V, const void *alpha, la_dtype io_dtype,
-                             int64_t B, int64_t H, int64_t T, int32_t d, int32_t dv, double eps, int32_t chunk,
-                             void *Y, void *S, void *z, la_dtype state_dtype, hipStream_t stream)
+la_status la_prefill_chunked_fm(const void *Q, const void *K, const void *V, const void *alpha, la_dtype io_dtype,
+                                int64_t B, int64_t H, int64_t T, int32_t d, int32_t dv, double eps, int32_t chunk,
+                                void *Y, void *S, void *z, la_dtype state_dtype, la_feature_map phi,
+                                hipStream_t stream)
 {
     if (!Q || !K || !V || !Y || !S || !z)
         return LA_ERR_NULL;
@@ -166,17 +174,58 @@ la_status la_prefill_chunked(const void *Q, const void *K, const void *V, const 
         return LA_ERR_SHAPE;
     if (any_alias({{Y, vy}, {S, sb}, {z, zb}}, {{Q, qk}, {K, qk}, {V, vy}, {alpha, alpha ? ab : 0}}))
         return LA_ERR_ALIAS;
+    if (!phi_ok(phi))
+        return LA_ERR_PHI;
 
-    la::PrefillArgs a{Q, K, V, alpha, heads, T, d, dv, eps, chunk, Y, S, z};
+    la::PrefillArgs a{Q, K, V, alpha, heads, T, d, dv, eps, chunk, Y, S, z, phi};
     (void)hipGetLastError();
     if (la::mfma_prefill_supported(io_dtype, d, dv, chunk))
         return launched(la::launch_prefill_mfma_bf16(a, stream));
     return launched(la::launch_prefill_general(a, io_dtype, stream));
 }
 
-la_status la_decode_step(const void *q, const void *k, const void *v, const void *alpha, la_dtype io_dtype,
-                         int64_t n_states, int32_t d, int32_t dv, double eps, void *y, void *S, void *z,
-                         la_dtype state_dtype, hipStream_t stream)
+la_status la_prefill_chunked(const void *Q, const void *K, const void *V, const void *alpha, la_dtype io_dtype,
+                             int64_t B, int64_t H, int64_t T, int32_t d, int32_t dv, double eps, int32_t chunk,
+                             void *Y, void *S, void *z, la_dtype state_dtype, hipStream_t stream)
+{
+    return la_prefill_chunked_fm(Q, K, V, alpha, io_dtype, B, H, T, d, dv, eps, chunk, Y, S, z, state_dtype,
+                                 LA_PHI_ELU1, stream);
+}
+
+la_status la_prefill_noncausal(const void *Q, const void *K, const void *V, la_dtype io_dtype, int64_t B, int64_t H,
+                               int64_t T, int32_t d, int32_t dv, double eps, void *Y, void *S, void *z,
+                               la_dtype state_dtype, la_feature_map phi, hipStream_t stream)
+{
+    if (!Q || !K || !V || !Y || !S || !z)
+        return LA_ERR_NULL;
+    if (B < 1 || H < 1 || T < 1 || d < 1 || dv < 1)
+        return LA_ERR_SHAPE;
+    if (!valid_pair(io_dtype, state_dtype))
+        return LA_ERR_DTYPE;
+    if (!eps_ok(eps))
+        return LA_ERR_EPS;
+    if (d > LA_MAX_WIDTH || dv > LA_MAX_WIDTH)
+        return LA_ERR_UNSUPPORTED;
+    int64_t heads, qk, vy, sb, zb;
+    const int64_t ei = dtype_bytes(io_dtype), es = dtype_bytes(state_dtype);
+    if (!mul_ok(B, H, &heads) || heads > INT32_MAX || !prod_ok({heads, T, d, ei}, &qk) ||
+        !prod_ok({heads, T, dv, ei}, &vy) || !prod_ok({heads, d, dv, es}, &sb) || !prod_ok({heads, d, es}, &zb))
+        return LA_ERR_SHAPE;
+    if (any_alias({{Y, vy}, {S, sb}, {z, zb}}, {{Q, qk}, {K, qk}, {V, vy}}))
+        return LA_ERR_ALIAS;
+    if (!phi_ok(phi))
+        return LA_ERR_PHI;
+
+    la::PrefillArgs a{Q, K, V, nullptr, heads, T, d, dv, eps, 0, Y, S, z, phi};
+    (void)hipGetLastError();
+    if (la::mfma_noncausal_supported(io_dtype, d, dv))
+        return launched(la::launch_noncausal_mfma_bf16(a, stream));
+    return launched(la::launch_noncausal_general(a, io_dtype, stream));
+}
+
+la_status la_decode_step_fm(const void *q, const void *k, const void *v, const void *alpha, la_dtype io_dtype,
+                            int64_t n_states, int32_t d, int32_t dv, double eps, void *y, void *S, void *z,
+                            la_dtype state_dtype, la_feature_map phi, hipStream_t stream)
 {
     if (!q || !k || !v || !y || !S || !z)
         return LA_ERR_NULL;
@@ -195,10 +244,20 @@ la_status la_decode_step(const void *q, const void *k, const void *v, const void
         return LA_ERR_SHAPE;
     if (any_alias({{y, vy}, {S, sb}, {z, zb}}, {{q, qk}, {k, qk}, {v, vy}, {alpha, alpha ? ab : 0}}))
         return LA_ERR_ALIAS;
+    if (!phi_ok(phi))
+        return LA_ERR_PHI;
 
-    la::DecodeArgs a{q, k, v, alpha, n_states, d, dv, eps, y, S, z};
+    la::DecodeArgs a{q, k, v, alpha, n_states, d, dv, eps, y, S, z, phi};
     (void)hipGetLastError();
     return launched(la::launch_decode(a, io_dtype, stream));
+}
+
+la_status la_decode_step(const void *q, const void *k, const void *v, const void *alpha, la_dtype io_dtype,
+                         int64_t n_states, int32_t d, int32_t dv, double eps, void *y, void *S, void *z,
+                         la_dtype state_dtype, hipStream_t stream)
+{
+    return la_decode_step_fm(q, k, v, alpha, io_dtype, n_states, d, dv, eps, y, S, z, state_dtype, LA_PHI_ELU1,
+                             stream);
 }
 
 la_status la_delta_decode_step(const void *q, const void *k, const void *v, const void *beta, la_dtype io_dtype,

@@ -4,18 +4,37 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "linattn.h"
+
 namespace la {
 
 typedef __bf16 bf16;
 
-// ---------------------------------------------------------------- feature map
-// phi(x) = ELU(x) + 1 with ELU's scale 1: x + 1 above zero, exp(x) at or below
-// (page "Linear attention：把历史写进状态", section "关键改写").  phi(0) = 1 from both
-// branches and phi(-inf) = 0 exactly.
-__device__ __forceinline__ float phi_accurate(float x) { return x > 0.f ? x + 1.f : expf(x); }
-__device__ __forceinline__ double phi_accurate(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
-// Hardware exp2 path; its few-ulp error is far below the bf16 rounding that follows.
-__device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+// ---------------------------------------------------------------- feature maps
+// FM is an la_feature_map value:
+//   LA_PHI_ELU1         ELU(x) + 1 with ELU's scale 1: x + 1 above zero, exp(x) at or
+//                       below (page "Linear attention：把历史写进状态", section "关键改写");
+//                       phi(0) = 1 from both branches and phi(-inf) = 0 exactly
+//   LA_PHI_RELU1        max(x, 0) + 1 (the positive map of the datawhalechina chapter
+//                       "Linear Attention and Recurrent State", Step 4)
+//   LA_PHI_RELU_EPS     max(x, 0) + 1e-5   (the switchable maps of the pluggable module
+//   LA_PHI_SIGMOID_EPS  sigmoid(x) + 1e-5   on the page "线性注意力架构演进", ai-master.cc)
+// Arithmetic in the type of x.
+__device__ __forceinline__ float exp_of(float x) { return expf(x); }
+__device__ __forceinline__ double exp_of(double x) { return exp(x); }
+
+template <int FM, typename T>
+__device__ __forceinline__ T phi_accurate(T x)
+{
+    if constexpr (FM == LA_PHI_RELU1)
+        return (x > T(0) ? x : T(0)) + T(1);
+    else if constexpr (FM == LA_PHI_RELU_EPS)
+        return (x > T(0) ? x : T(0)) + T(1e-5);
+    else if constexpr (FM == LA_PHI_SIGMOID_EPS)
+        return T(1) / (T(1) + exp_of(-x)) + T(1e-5);
+    else
+        return x > T(0) ? x + T(1) : exp_of(x);
+}
 
 // ---------------------------------------------------------------- io conversions
 template <typename TA, typename TI>

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <stdint.h>
+#include <type_traits>
 #include <hip/hip_runtime_api.h>
 
 #include "linattn.h"
@@ -16,6 +17,7 @@ struct PrefillArgs {
     double eps;
     int32_t chunk;
     void *Y, *S, *z;
+    int phi = LA_PHI_ELU1;  // an la_feature_map
 };
 
 struct DecodeArgs {
@@ -24,6 +26,7 @@ struct DecodeArgs {
     int32_t d, dv;
     double eps;
     void *y, *S, *z;
+    int phi = LA_PHI_ELU1;  // an la_feature_map
 };
 
 struct DeltaArgs {
@@ -33,6 +36,24 @@ struct DeltaArgs {
     void *y, *S;
 };
 
+// Calls f(std::integral_constant<int, FM>{}) for the feature map `phi` (an
+// la_feature_map the C ABI has already checked), so launchers pick a kernel
+// instantiation per map.
+template <typename F>
+hipError_t dispatch_feature_map(int phi, F &&f)
+{
+    switch (phi) {
+    case LA_PHI_RELU1:
+        return f(std::integral_constant<int, LA_PHI_RELU1>{});
+    case LA_PHI_RELU_EPS:
+        return f(std::integral_constant<int, LA_PHI_RELU_EPS>{});
+    case LA_PHI_SIGMOID_EPS:
+        return f(std::integral_constant<int, LA_PHI_SIGMOID_EPS>{});
+    default:
+        return f(std::integral_constant<int, LA_PHI_ELU1>{});
+    }
+}
+
 // Each launcher enqueues its kernels on `stream` and returns the HIP status of
 // the launch (hipSuccess or the runtime's refusal).  Arguments are already valid.
 hipError_t launch_state_init(void *S, void *z, int64_t n_states, int32_t r, int32_t dv,
@@ -40,9 +61,14 @@ hipError_t launch_state_init(void *S, void *z, int64_t n_states, int32_t r, int3
 hipError_t launch_prefill_general(const PrefillArgs &a, la_dtype io_dtype, hipStream_t stream);
 hipError_t launch_prefill_mfma_bf16(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, la_dtype io_dtype, hipStream_t stream);
+// Non-causal form (PrefillArgs without alpha and chunk): S, z += the whole sequence,
+// then every query reads the final state.
+hipError_t launch_noncausal_general(const PrefillArgs &a, la_dtype io_dtype, hipStream_t stream);
+hipError_t launch_noncausal_mfma_bf16(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_delta_decode(const DeltaArgs &a, la_dtype io_dtype, hipStream_t stream);
 
 // True when the bf16 MFMA prefill kernel handles the request.
 bool mfma_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk);
+bool mfma_noncausal_supported(la_dtype io_dtype, int32_t d, int32_t dv);
 
 }  // namespace la

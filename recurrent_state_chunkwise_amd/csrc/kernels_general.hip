@@ -1,10 +1,11 @@
 // General kernels: state initialisation, the general chunked prefill (any d, dv <= 128,
-// chunk <= 128, f64/f32/bf16 io, arithmetic in the state dtype) and the batched
-// decode step.
+// chunk <= 128, f64/f32/bf16 io, arithmetic in the state dtype), the general non-causal
+// form and the batched decode step.
 //
 // The operation is the one of page "Linear attention：把历史写进状态"
 // (hs-black.github.io): phi = ELU+1, gated write S = a*S + k~ v^T, z = a*z + k~, then
-// y = q~^T S / (q~^T z + eps).
+// y = q~^T S / (q~^T z + eps).  Every kernel takes the feature map FM (an
+// la_feature_map) as a template parameter.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -80,7 +81,7 @@ size_t general_prefill_lds_bytes(int d, int slice)
 // the gates since the last zero gate (lg) and the position of that zero gate (zp):
 // the product of gates over (i, j] is 0 when a zero gate lies in (i, j], else
 // exp(lg[j] - lg[i]).
-template <typename TI, typename TA>
+template <typename TI, typename TA, int FM>
 __global__ __launch_bounds__(kThreads) void prefill_general_kernel(
     const TI *__restrict__ Q, const TI *__restrict__ K, const TI *__restrict__ V, const TA *__restrict__ alpha,
     int64_t T, int d, int dv, int slice, TA eps, int chunk, TI *__restrict__ Y, TA *__restrict__ S,
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void prefill_general_kernel(
             const int rb = min(kRB, n - j0);
             for (int e = tid; e < rb * d; e += kThreads) {
                 const int jj = e / d, f = e - jj * d;
-                Qt[jj * dp + f] = phi_accurate(to_acc<TA>(Qh[(t0 + j0 + jj) * d + f]));
+                Qt[jj * dp + f] = phi_accurate<FM>(to_acc<TA>(Qh[(t0 + j0 + jj) * d + f]));
             }
             __syncthreads();
 
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void prefill_general_kernel(
                 __syncthreads();
                 for (int e = tid; e < ib * d; e += kThreads) {
                     const int ii = e / d, f = e - ii * d;
-                    Kt[ii * dp + f] = phi_accurate(to_acc<TA>(Kh[(t0 + i0 + ii) * d + f]));
+                    Kt[ii * dp + f] = phi_accurate<FM>(to_acc<TA>(Kh[(t0 + i0 + ii) * d + f]));
                 }
                 for (int e = tid; e < ib * nc; e += kThreads) {
                     const int ii = e / nc, c = e - ii * nc;
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void prefill_general_kernel(
             __syncthreads();
             for (int e = tid; e < ib * d; e += kThreads) {
                 const int ii = e / d, f = e - ii * d;
-                Kt[ii * dp + f] = phi_accurate(to_acc<TA>(Kh[(t0 + i0 + ii) * d + f]));
+                Kt[ii * dp + f] = phi_accurate<FM>(to_acc<TA>(Kh[(t0 + i0 + ii) * d + f]));
             }
             for (int e = tid; e < ib * nc; e += kThreads) {
                 const int ii = e / nc, c = e - ii * nc;
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void prefill_general_kernel(
             zh[f] = zs[f];
 }
 
-template <typename TI, typename TA>
+template <typename TI, typename TA, int FM>
 hipError_t launch_general_typed(const PrefillArgs &a, hipStream_t stream)
 {
     // widest value slice whose working set fits a 64 KiB LDS budget
@@ -315,10 +316,156 @@ hipError_t launch_general_typed(const PrefillArgs &a, hipStream_t stream)
         slice /= 2;
     const size_t lds = general_prefill_lds_bytes<TA>(a.d, slice);
     const unsigned n_slices = (unsigned)((a.dv + slice - 1) / slice);
-    prefill_general_kernel<TI, TA><<<dim3((unsigned)a.n_heads, n_slices), dim3(kThreads), lds, stream>>>(
+    prefill_general_kernel<TI, TA, FM><<<dim3((unsigned)a.n_heads, n_slices), dim3(kThreads), lds, stream>>>(
         static_cast<const TI *>(a.Q), static_cast<const TI *>(a.K), static_cast<const TI *>(a.V),
         static_cast<const TA *>(a.alpha), a.T, a.d, a.dv, slice, static_cast<TA>(a.eps), a.chunk,
         static_cast<TI *>(a.Y), static_cast<TA *>(a.S), static_cast<TA *>(a.z));
+    return hipGetLastError();
+}
+
+// ===================================================================== general non-causal form
+template <typename TA>
+size_t noncausal_general_lds_bytes(int d, int slice)
+{
+    const int dp = d + 1;
+    return sizeof(TA) * (size_t)(d * slice + d + kRB * dp + kIB * dp + kIB * slice + kRB);
+}
+
+// One workgroup per (sequence, slice of value columns).  First the whole sequence is
+// written into the workgroup's slice of the state (and into all of z, which every
+// slice needs), kIB tokens at a time; the state goes back to the caller; then every
+// query is read against it, kRB rows at a time.  Slice 0 writes z.
+template <typename TI, typename TA, int FM>
+__global__ __launch_bounds__(kThreads) void noncausal_general_kernel(
+    const TI *__restrict__ Q, const TI *__restrict__ K, const TI *__restrict__ V, int64_t T, int d, int dv,
+    int slice, TA eps, TI *__restrict__ Y, TA *__restrict__ S, TA *__restrict__ z)
+{
+    const int tid = threadIdx.x;
+    const int64_t h = blockIdx.x;
+    const int c0 = blockIdx.y * slice;
+    const int nc = min(slice, dv - c0);
+    const int dp = d + 1;
+
+    const TI *Qh = Q + h * T * d;
+    const TI *Kh = K + h * T * d;
+    const TI *Vh = V + h * T * dv;
+    TI *Yh = Y + h * T * dv;
+    TA *Sh = S + h * (int64_t)d * dv;
+    TA *zh = z + h * d;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    TA *Ss = reinterpret_cast<TA *>(smem_raw);  // [d][slice] the full-sequence state slice
+    TA *zs = Ss + d * slice;                     // [d]
+    TA *Qt = zs + d;                             // [kRB][dp] phi(q) rows
+    TA *Kt = Qt + kRB * dp;                      // [kIB][dp] phi(k) rows
+    TA *Vt = Kt + kIB * dp;                      // [kIB][slice]
+    TA *den_s = Vt + kIB * slice;                // [kRB]
+
+    // ---------------- write: S_in + sum of k~ v^T, z_in + sum of k~
+    TA sreg[kStateRegs];
+#pragma unroll
+    for (int p = 0; p < kStateRegs; ++p) {
+        const int e = tid + p * kThreads;
+        sreg[p] = TA(0);
+        if (e < d * nc) {
+            const int f = e / nc, c = e - f * nc;
+            sreg[p] = Sh[(int64_t)f * dv + c0 + c];
+        }
+    }
+    TA zreg = tid < d ? zh[tid] : TA(0);
+    for (int64_t i0 = 0; i0 < T; i0 += kIB) {
+        const int ib = (int)min((int64_t)kIB, T - i0);
+        __syncthreads();
+        for (int e = tid; e < ib * d; e += kThreads) {
+            const int ii = e / d, f = e - ii * d;
+            Kt[ii * dp + f] = phi_accurate<FM>(to_acc<TA>(Kh[(i0 + ii) * d + f]));
+        }
+        for (int e = tid; e < ib * nc; e += kThreads) {
+            const int ii = e / nc, c = e - ii * nc;
+            Vt[ii * slice + c] = to_acc<TA>(Vh[(i0 + ii) * dv + c0 + c]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < kStateRegs; ++p) {
+            const int e = tid + p * kThreads;
+            if (e < d * nc) {
+                const int f = e / nc, c = e - f * nc;
+                TA acc = sreg[p];
+                for (int ii = 0; ii < ib; ++ii)
+                    acc += Kt[ii * dp + f] * Vt[ii * slice + c];
+                sreg[p] = acc;
+            }
+        }
+        if (tid < d) {
+            TA acc = zreg;
+            for (int ii = 0; ii < ib; ++ii)
+                acc += Kt[ii * dp + tid];
+            zreg = acc;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < kStateRegs; ++p) {
+        const int e = tid + p * kThreads;
+        if (e < d * nc) {
+            const int f = e / nc, c = e - f * nc;
+            Ss[f * slice + c] = sreg[p];
+            Sh[(int64_t)f * dv + c0 + c] = sreg[p];
+        }
+    }
+    if (tid < d) {
+        zs[tid] = zreg;
+        if (blockIdx.y == 0)
+            zh[tid] = zreg;
+    }
+
+    // ---------------- read: every query against the full state
+    for (int64_t j0 = 0; j0 < T; j0 += kRB) {
+        const int rb = (int)min((int64_t)kRB, T - j0);
+        __syncthreads();
+        for (int e = tid; e < rb * d; e += kThreads) {
+            const int jj = e / d, f = e - jj * d;
+            Qt[jj * dp + f] = phi_accurate<FM>(to_acc<TA>(Qh[(j0 + jj) * d + f]));
+        }
+        __syncthreads();
+        if (tid < rb) {
+            TA acc = 0;
+            for (int f = 0; f < d; ++f)
+                acc += Qt[tid * dp + f] * zs[f];
+            den_s[tid] = acc;
+        }
+        TA num[kPairs];
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p) {
+            num[p] = TA(0);
+            const int e = tid + p * kThreads, jj = e / slice, c = e - jj * slice;
+            if (jj < rb && c < nc) {
+                TA acc = 0;
+                for (int f = 0; f < d; ++f)
+                    acc += Qt[jj * dp + f] * Ss[f * slice + c];
+                num[p] = acc;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p) {
+            const int e = tid + p * kThreads, jj = e / slice, c = e - jj * slice;
+            if (jj < rb && c < nc)
+                Yh[(j0 + jj) * dv + c0 + c] = from_acc<TI>(num[p] / (den_s[jj] + eps));
+        }
+    }
+}
+
+template <typename TI, typename TA, int FM>
+hipError_t launch_noncausal_typed(const PrefillArgs &a, hipStream_t stream)
+{
+    int slice = a.dv < kMaxSlice ? a.dv : kMaxSlice;
+    while (slice > 1 && noncausal_general_lds_bytes<TA>(a.d, slice) > 65536)
+        slice /= 2;
+    const size_t lds = noncausal_general_lds_bytes<TA>(a.d, slice);
+    const unsigned n_slices = (unsigned)((a.dv + slice - 1) / slice);
+    noncausal_general_kernel<TI, TA, FM><<<dim3((unsigned)a.n_heads, n_slices), dim3(kThreads), lds, stream>>>(
+        static_cast<const TI *>(a.Q), static_cast<const TI *>(a.K), static_cast<const TI *>(a.V), a.T, a.d, a.dv,
+        slice, static_cast<TA>(a.eps), static_cast<TI *>(a.Y), static_cast<TA *>(a.S), static_cast<TA *>(a.z));
     return hipGetLastError();
 }
 
@@ -331,7 +478,7 @@ constexpr int kDecodeThreads = 512;
 // thread's rows are loaded before any is used.
 // Each state is touched once per step, so its loads and stores are marked
 // non-temporal to keep it from displacing other lines in the caches.
-template <typename TI, typename TA, int VEC>
+template <typename TI, typename TA, int VEC, int FM>
 __global__ __launch_bounds__(kDecodeThreads) void decode_w128_kernel(
     const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v, const TA *__restrict__ alpha,
     TA eps, TI *__restrict__ y, TA *__restrict__ S, TA *__restrict__ z)
@@ -353,8 +500,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_w128_kernel(
         s[i] = __builtin_nontemporal_load(&Sv[(rg + i * NRG) * NCG + cg]);
     const TA zf = tid < D ? z[n * D + tid] : TA(0);
     if (tid < D) {
-        kf[tid] = phi_accurate(to_acc<TA>(k[n * D + tid]));
-        qf[tid] = phi_accurate(to_acc<TA>(q[n * D + tid]));
+        kf[tid] = phi_accurate<FM>(to_acc<TA>(k[n * D + tid]));
+        qf[tid] = phi_accurate<FM>(to_acc<TA>(q[n * D + tid]));
         vs[tid] = to_acc<TA>(v[n * DV + tid]);
     }
     const TA a = alpha ? alpha[n] : TA(1);
@@ -403,7 +550,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_w128_kernel(
 }
 
 // Any d, dv <= 128: thread (rg, c) owns column c of rows rg, rg + nrg, ...
-template <typename TI, typename TA>
+template <typename TI, typename TA, int FM>
 __global__ __launch_bounds__(kThreads) void decode_general_kernel(
     const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v, const TA *__restrict__ alpha,
     int d, int dv, TA eps, TI *__restrict__ y, TA *__restrict__ S, TA *__restrict__ z)
@@ -414,8 +561,8 @@ __global__ __launch_bounds__(kThreads) void decode_general_kernel(
     const int tid = threadIdx.x;
     const int64_t n = blockIdx.x;
     if (tid < d) {
-        kf[tid] = phi_accurate(to_acc<TA>(k[n * d + tid]));
-        qf[tid] = phi_accurate(to_acc<TA>(q[n * d + tid]));
+        kf[tid] = phi_accurate<FM>(to_acc<TA>(k[n * d + tid]));
+        qf[tid] = phi_accurate<FM>(to_acc<TA>(q[n * d + tid]));
     }
     if (tid < dv)
         vs[tid] = to_acc<TA>(v[n * dv + tid]);
@@ -456,18 +603,18 @@ __global__ __launch_bounds__(kThreads) void decode_general_kernel(
     }
 }
 
-template <typename TI, typename TA>
+template <typename TI, typename TA, int FM>
 hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t stream)
 {
     constexpr int VEC = 16 / sizeof(TA);
     const bool aligned = (reinterpret_cast<uintptr_t>(a.S) % 16) == 0;
     if (a.d == 128 && a.dv == 128 && aligned) {
-        decode_w128_kernel<TI, TA, VEC><<<dim3((unsigned)a.n_states), dim3(kDecodeThreads), 0, stream>>>(
+        decode_w128_kernel<TI, TA, VEC, FM><<<dim3((unsigned)a.n_states), dim3(kDecodeThreads), 0, stream>>>(
             static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
             static_cast<const TA *>(a.alpha), static_cast<TA>(a.eps), static_cast<TI *>(a.y),
             static_cast<TA *>(a.S), static_cast<TA *>(a.z));
     } else {
-        decode_general_kernel<TI, TA><<<dim3((unsigned)a.n_states), dim3(kThreads), 0, stream>>>(
+        decode_general_kernel<TI, TA, FM><<<dim3((unsigned)a.n_states), dim3(kThreads), 0, stream>>>(
             static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
             static_cast<const TA *>(a.alpha), a.d, a.dv, static_cast<TA>(a.eps), static_cast<TI *>(a.y),
             static_cast<TA *>(a.S), static_cast<TA *>(a.z));
@@ -489,26 +636,47 @@ hipError_t launch_state_init(void *S, void *z, int64_t n_states, int32_t r, int3
 
 hipError_t launch_prefill_general(const PrefillArgs &a, la_dtype io_dtype, hipStream_t stream)
 {
-    switch (io_dtype) {
-    case LA_F64:
-        return launch_general_typed<double, double>(a, stream);
-    case LA_F32:
-        return launch_general_typed<float, float>(a, stream);
-    default:
-        return launch_general_typed<bf16, float>(a, stream);
-    }
+    return dispatch_feature_map(a.phi, [&](auto fm) {
+        constexpr int FM = decltype(fm)::value;
+        switch (io_dtype) {
+        case LA_F64:
+            return launch_general_typed<double, double, FM>(a, stream);
+        case LA_F32:
+            return launch_general_typed<float, float, FM>(a, stream);
+        default:
+            return launch_general_typed<bf16, float, FM>(a, stream);
+        }
+    });
+}
+
+hipError_t launch_noncausal_general(const PrefillArgs &a, la_dtype io_dtype, hipStream_t stream)
+{
+    return dispatch_feature_map(a.phi, [&](auto fm) {
+        constexpr int FM = decltype(fm)::value;
+        switch (io_dtype) {
+        case LA_F64:
+            return launch_noncausal_typed<double, double, FM>(a, stream);
+        case LA_F32:
+            return launch_noncausal_typed<float, float, FM>(a, stream);
+        default:
+            return launch_noncausal_typed<bf16, float, FM>(a, stream);
+        }
+    });
 }
 
 hipError_t launch_decode(const DecodeArgs &a, la_dtype io_dtype, hipStream_t stream)
 {
-    switch (io_dtype) {
-    case LA_F64:
-        return launch_decode_typed<double, double>(a, stream);
-    case LA_F32:
-        return launch_decode_typed<float, float>(a, stream);
-    default:
-        return launch_decode_typed<bf16, float>(a, stream);
-    }
+    return dispatch_feature_map(a.phi, [&](auto fm) {
+        constexpr int FM = decltype(fm)::value;
+        switch (io_dtype) {
+        case LA_F64:
+            return launch_decode_typed<double, double, FM>(a, stream);
+        case LA_F32:
+            return launch_decode_typed<float, float, FM>(a, stream);
+        default:
+            return launch_decode_typed<bf16, float, FM>(a, stream);
+        }
+    });
 }
 
 }  // namespace la

@@ -79,11 +79,21 @@ __device__ __forceinline__ void unpack8(uint4 u, float *f)
     }
 }
 
-// phi = ELU + 1 as the median of (x + 1, e^x, 1): x + 1 for x > 0 (where e^x > x + 1 > 1)
-// and e^x for x <= 0 (where x + 1 <= e^x <= 1); e^x on the hardware exp2
+// The feature map on the values the kernels stage as bf16 operands, where the few-ulp
+// error of the hardware exp2 and reciprocal is far below the bf16 rounding that follows.
+// ELU + 1 is the median of (x + 1, e^x, 1): x + 1 for x > 0 (where e^x > x + 1 > 1) and
+// e^x for x <= 0 (where x + 1 <= e^x <= 1).  The other maps are those of la_feature_map.
+template <int FM>
 __device__ __forceinline__ float phi(float x)
 {
-    return __builtin_amdgcn_fmed3f(x + 1.f, __builtin_amdgcn_exp2f(x * kLog2e), 1.f);
+    if constexpr (FM == LA_PHI_RELU1)
+        return __builtin_fmaxf(x, 0.f) + 1.f;
+    else if constexpr (FM == LA_PHI_RELU_EPS)
+        return __builtin_fmaxf(x, 0.f) + 1e-5f;
+    else if constexpr (FM == LA_PHI_SIGMOID_EPS)
+        return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) + 1e-5f;
+    else
+        return __builtin_amdgcn_fmed3f(x + 1.f, __builtin_amdgcn_exp2f(x * kLog2e), 1.f);
 }
 
 // Buffer resources (gfx9 raw buffers): an access at or past num_records bytes reads
@@ -166,7 +176,7 @@ __device__ __forceinline__ float *slot_ptr(const Args &a, int64_t head, int p)
 // Pass 3 with 8 waves that stage and multiply in turn (the form used at chunk 128,
 // where two buffers of every tile do not fit in LDS): outputs from the entering state;
 // the last segment writes S, z.
-template <int C, bool GATED>
+template <int C, bool GATED, int FM>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 {
     typedef Cfg<C> G;
@@ -302,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
             bf16x8 kb;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const float f = phi(x[s]);
+                const float f = phi<FM>(x[s]);
                 kb[s] = static_cast<bf16>(f);
                 if (GATED)
                     x[s] = w * f;
@@ -343,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
             bf16x8 qb;
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                qb[s] = static_cast<bf16>(phi(x[s]));
+                qb[s] = static_cast<bf16>(phi<FM>(x[s]));
             *reinterpret_cast<bf16x8 *>(&sm.Qs[qk_off(j, fg * 8)]) = qb;
         }
     };
@@ -638,7 +648,7 @@ __device__ __forceinline__ void wg_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <bool GATED>
+template <bool GATED, int FM>
 __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
 {
     constexpr int C = kPcC;
@@ -728,7 +738,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 bf16x8 qb;
 #pragma unroll
                 for (int s = 0; s < 8; ++s)
-                    qb[s] = static_cast<bf16>(phi(x[s]));
+                    qb[s] = static_cast<bf16>(phi<FM>(x[s]));
                 *reinterpret_cast<bf16x8 *>(&sm.Qs[buf][pr_off(j, fg * 8)]) = qb;
                 *reinterpret_cast<uint4 *>(&sm.Vs[buf][pr_off(j, fg * 8)]) = rv[p];
             }
@@ -747,7 +757,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 const float w = j >= n ? 0.f : (GATED ? pair_decay(gs, n - 1, j) : 1.f);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    const float f = phi(x[s]);
+                    const float f = phi<FM>(x[s]);
                     kb[s] = static_cast<bf16>(f);
                     if (GATED)
                         kwb[s] = static_cast<bf16>(w * f);
@@ -1038,9 +1048,13 @@ struct alignas(16) SumSmem {
     alignas(16) int zp[3][kPcC];
 };
 
-template <bool GATED>
+// NONCAUSAL (ungated): every segment's map is needed, including the last one's, and it
+// goes to the segment's own slot; with a single segment it is added straight into the
+// caller's S and z.
+template <bool GATED, int FM, bool NONCAUSAL>
 __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
 {
+    static_assert(!(GATED && NONCAUSAL), "the non-causal form has no gate");
     constexpr int C = kPcC;
     typedef Cfg<C> G;
     __shared__ SumSmem<GATED> sm;
@@ -1053,10 +1067,10 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
 
     const int64_t head = blockIdx.x / a.nseg;
     const int seg = blockIdx.x % a.nseg;
-    if (seg == a.nseg - 1)
+    if (!NONCAUSAL && seg == a.nseg - 1)
         return;  // the last segment's map is never needed
     const int64_t s0 = (int64_t)seg * a.seg_len;
-    const int64_t len = a.seg_len;
+    const int64_t len = seg == a.nseg - 1 ? a.T - s0 : a.seg_len;
     const int n_chunks = (int)((len + C - 1) / C);
     const int n_steps = (n_chunks + 1) & ~1;  // both roles walk an even number of chunk steps
     auto chunk_len = [&](int c) { return (int)min((int64_t)C, len - (int64_t)c * C); };
@@ -1117,7 +1131,7 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                 bf16x8 kb;
 #pragma unroll
                 for (int s = 0; s < 8; ++s)
-                    kb[s] = static_cast<bf16>(GATED ? w * phi(x[s]) : phi(x[s]));
+                    kb[s] = static_cast<bf16>(GATED ? w * phi<FM>(x[s]) : phi<FM>(x[s]));
                 uint4 u = *reinterpret_cast<uint4 *>(&kb);
                 if (!GATED && j >= n)
                     u = make_uint4(0u, 0u, 0u, 0u);
@@ -1211,20 +1225,28 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
         wg_barrier();  // chunk i folded
     }
 
-    // the map goes to the next segment's slot: S, z, then the product of the gates
-    float *Sout = slot_ptr(a, head, seg + 1);
+    // causal: the map goes to the next segment's slot: S, z, then the product of the gates
+    float *Sout = slot_ptr(a, head, NONCAUSAL ? seg : seg + 1);
     float *zout = Sout + kD * kD;
-    if (tid == 0)
+    bool add_in = false;
+    if (NONCAUSAL && a.nseg == 1) {
+        Sout = a.S + head * kD * kD;
+        zout = a.z + head * kD;
+        add_in = true;
+    }
+    if (!NONCAUSAL && tid == 0)
         Sout[kD * kD + kD] = g_seg;
 #pragma unroll
     for (int tf = 0; tf < 8; ++tf)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Sout[(tf * 16 + lg4 * 4 + r) * kD + cw] = sacc[tf][r];
+        for (int r = 0; r < 4; ++r) {
+            float *o = &Sout[(tf * 16 + lg4 * 4 + r) * kD + cw];
+            *o = sacc[tf][r] + (add_in ? *o : 0.f);
+        }
     if (lr == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            zout[fw + r] = zr[r];
+            zout[fw + r] = zr[r] + (add_in ? zout[fw + r] : 0.f);
     }
 }
 
@@ -1260,14 +1282,14 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(Args a)
     }
 }
 
-template <int C, bool GATED>
+template <int C, bool GATED, int FM>
 hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)(n_heads * a.nseg);
     if (a.nseg > 1) {
         // pass 1 walks 64-token chunks whatever the caller's chunk: its chunking only
         // changes the rounding of the segment maps
-        summary_pc_kernel<GATED><<<dim3(blocks), dim3(kSumThreads), 0, stream>>>(a);
+        summary_pc_kernel<GATED, FM, false><<<dim3(blocks), dim3(kSumThreads), 0, stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -1277,19 +1299,278 @@ hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
             return e;
     }
     if constexpr (C == kPcC)
-        prefill_pc_kernel<GATED><<<dim3(blocks), dim3(kPcThreads), 0, stream>>>(a);
+        prefill_pc_kernel<GATED, FM><<<dim3(blocks), dim3(kPcThreads), 0, stream>>>(a);
     else
-        chunk_kernel<C, GATED><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
+        chunk_kernel<C, GATED, FM><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+// ============================================================================ non-causal form
+// Non-causal form (page "线性注意力架构演进", ai-master.cc: K~^T V and the key sum are
+// formed once and every query reads them):
+//   pass 1  summary_pc_kernel<false, FM, true>: each (sequence, segment) folds its tokens
+//           into (dS, dz) in its own slot (a single segment adds into S, z directly);
+//   pass 2  segment_sum_kernel: S = S_in + sum of the slots, same for z;
+//   pass 3  noncausal_readout_kernel: y_t = q~_t^T S / (q~_t^T z + eps) for every t.
+
+// S_out = S_in + sum over segments of dS (and z likewise), in the caller's S and z.
+__global__ __launch_bounds__(256) void segment_sum_kernel(Args a)
+{
+    const int64_t head = blockIdx.y;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= kD * kD + kD)
+        return;
+    float *dst = e < kD * kD ? &a.S[head * kD * kD + e] : &a.z[head * kD + (e - kD * kD)];
+    float run = *dst;
+    constexpr int kBatch = 8;
+    for (int p0 = 0; p0 < a.nseg; p0 += kBatch) {
+        float d[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            d[q] = p0 + q < a.nseg ? slot_ptr(a, head, p0 + q)[e] : 0.f;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q)
+            run += d[q];
+    }
+    *dst = run;
+}
+
+// Read-out: one workgroup of 8 waves per (sequence, block of kNcBlockTokens tokens).
+// The workgroup converts S to bf16 once, transposed into LDS, with z split into bf16
+// high and low parts (so the denominator keeps about 16 bits of z); every wave then
+// keeps S^T in registers as 32 MFMA A-operands and streams 16-token tiles of Q through
+// v_mfma_f32_16x16x32_bf16: the transposed numerator N^T = S^T Q~^T and the
+// denominator 1 z^T Q~^T, so a lane ends with eight adjacent output columns of one
+// token and that token's denominator.
+// Q and Y move between HBM and registers as whole 256-byte rows (16 lanes per row,
+// four rows per instruction) and are rearranged through a wave-private LDS tile into
+// and out of the MFMA layouts; the tiles' 16-byte granules are XOR-swizzled by row so
+// that both sides of the rearrangement are free of bank conflicts.  The first tiles'
+// loads are issued before the staging, and three register sets keep up to three
+// tiles in flight per wave.
+constexpr int kNcWaves = 8;
+constexpr int kNcThreads = 64 * kNcWaves;
+constexpr int kNcTilesPerWave = 8;
+constexpr int kNcSets = 3;
+constexpr int kNcBlockTokens = 16 * kNcWaves * kNcTilesPerWave;
+constexpr int kStRow = kD + 8;  // bf16 row stride of S^T in LDS (272 bytes)
+
+// byte offset of 16-byte granule `gran` of row `row` in a swizzled 16 x 256-byte tile
+__device__ __forceinline__ int sw_off(int row, int gran) { return row * 256 + ((gran ^ row) & 15) * 16; }
+
+template <int FM>
+__global__ __launch_bounds__(kNcThreads) void noncausal_readout_kernel(Args a, int blocks_per_head)
+{
+    __shared__ __align__(16) bf16 St[kD * kStRow];             // St[f][r] = S[r][f]
+    __shared__ __align__(16) bf16x8 Zs[2][4][4];                // [hi/lo][k-step][lane group]: z of 8 features
+    __shared__ __align__(16) unsigned char Qt[kNcWaves][4096];  // per wave: a Q tile, swizzled
+    __shared__ __align__(16) unsigned char Yt[kNcWaves][4096];  // per wave: a Y tile, swizzled
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int m = lane & 15;  // A-operand row / B-operand column (token) / output column
+    const int g = lane >> 4;  // lane group: k = 8g .. 8g+7 of each 32-wide step
+    const int64_t head = blockIdx.x / blocks_per_head;
+    const int64_t t0 = (int64_t)(blockIdx.x % blocks_per_head) * kNcBlockTokens;
+    const int len = (int)min((int64_t)kNcBlockTokens, a.T - t0);
+
+    // this block's rows of Q and Y; reads past the end give zeros, writes are dropped
+    const int64_t row0 = head * a.T + t0;
+    const rsrc_t rQ = make_rsrc(a.Q + row0 * kD, (int64_t)len * kD * 2);
+    const rsrc_t rY = make_rsrc(a.Y + row0 * kD, (int64_t)len * kD * 2);
+    const float eps = a.eps;
+    unsigned char *qt = Qt[wave];
+    unsigned char *yt = Yt[wave];
+    auto tile_of = [&](int it) { return wave + it * kNcWaves; };  // tiles wave, wave + 8, ...
+    // row-major transfers: lane takes granule m of rows g, g + 4, g + 8, g + 12
+    auto load = [&](int tile, uint4 (&q)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q[i] = bload16(rQ, ((tile * 16 + 4 * i + g) * kD + 8 * m) * 2);
+    };
+    uint4 qr[kNcSets][4];
+#pragma unroll
+    for (int it = 0; it < kNcSets; ++it)
+        load(tile_of(it), qr[it]);
+
+    // S (fp32, [r][f]) -> bf16 S^T in LDS: a thread takes rows r, r+1 of four columns
+    const float *Sh = a.S + head * kD * kD;
+    for (int e = tid; e < kD * kD / 8; e += kNcThreads) {
+        const int r = 2 * (e >> 5), f = 4 * (e & 31);
+        const float4 s0 = *reinterpret_cast<const float4 *>(&Sh[r * kD + f]);
+        const float4 s1 = *reinterpret_cast<const float4 *>(&Sh[(r + 1) * kD + f]);
+        const float lo[4] = {s0.x, s0.y, s0.z, s0.w}, hi[4] = {s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16x2 pr;
+            pr[0] = static_cast<bf16>(lo[i]);
+            pr[1] = static_cast<bf16>(hi[i]);
+            *reinterpret_cast<bf16x2 *>(&St[(f + i) * kStRow + r]) = pr;
+        }
+    }
+    // z as A operands (every row the same): k-step ks, lane group gg holds features
+    // 32 ks + 8 gg .. + 7
+    if (tid < 16) {
+        const int ks = tid >> 2, gg = tid & 3;
+        const float *zh = a.z + head * kD + 32 * ks + 8 * gg;
+        const float4 z0 = *reinterpret_cast<const float4 *>(zh);
+        const float4 z1 = *reinterpret_cast<const float4 *>(zh + 4);
+        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        bf16x8 h, l;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            h[s] = static_cast<bf16>(zv[s]);
+            l[s] = static_cast<bf16>(zv[s] - static_cast<float>(h[s]));
+        }
+        Zs[0][ks][gg] = h;
+        Zs[1][ks][gg] = l;
+    }
+    __syncthreads();
+
+    // S^T operands: tile ft, row m holds column f(ft, m) = 32 (ft/2) + 8 (m/4) + 4 (ft%2) + m%4,
+    // so output row 4g + i of tiles 2j and 2j+1 are columns 32 j + 8 g + 0..7 (granule 4j + g)
+    bf16x8 sa[8][4];
+#pragma unroll
+    for (int ft = 0; ft < 8; ++ft) {
+        const int f = 32 * (ft >> 1) + 8 * (m >> 2) + 4 * (ft & 1) + (m & 3);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            sa[ft][ks] = *reinterpret_cast<const bf16x8 *>(&St[f * kStRow + 32 * ks + 8 * g]);
+    }
+
+    auto compute = [&](int tile, const uint4 (&q)[4]) {
+        // rows into the wave's Q tile, then the B operands: token m, granule 4 ks + g
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4 *>(&qt[sw_off(4 * i + g, m)]) = q[i];
+        bf16x8 qb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float x[8];
+            unpack8(*reinterpret_cast<const uint4 *>(&qt[sw_off(m, 4 * ks + g)]), x);
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                qb[ks][s] = static_cast<bf16>(phi<FM>(x[s]));
+        }
+        f32x4 acc[8], den = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ft = 0; ft < 8; ++ft)
+            acc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int ft = 0; ft < 8; ++ft)
+                acc[ft] = mfma(sa[ft][ks], qb[ks], acc[ft]);
+            den = mfma(Zs[0][ks][g], qb[ks], den);
+            den = mfma(Zs[1][ks][g], qb[ks], den);
+        }
+        const float rd = 1.f / (den[0] + eps);
+        // token m's columns 32 j + 8 g .. + 7 into the wave's Y tile, then out as rows
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8 yb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                yb[i] = static_cast<bf16>(acc[2 * j][i] * rd);
+                yb[4 + i] = static_cast<bf16>(acc[2 * j + 1][i] * rd);
+            }
+            *reinterpret_cast<bf16x8 *>(&yt[sw_off(m, 4 * j + g)]) = yb;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(&yt[sw_off(4 * i + g, m)]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, u),
+                                                   rY, ((tile * 16 + 4 * i + g) * kD + 8 * m) * 2, 0, 0);
+        }
+    };
+
+    // tile it is computed from set it % kNcSets, which is then refilled with tile
+    // it + kNcSets; tiles past the block compute nothing (loads past it read zeros)
+    const int n_tiles = (len + 15) / 16;
+#pragma unroll
+    for (int it = 0; it < kNcTilesPerWave; ++it) {
+        if (tile_of(it) < n_tiles)
+            compute(tile_of(it), qr[it % kNcSets]);
+        if (it + kNcSets < kNcTilesPerWave)
+            load(tile_of(it + kNcSets), qr[it % kNcSets]);
+    }
+}
+
+template <int FM>
+hipError_t launch_nc(const Args &a, int64_t n_heads, hipStream_t stream)
+{
+    summary_pc_kernel<false, FM, true><<<dim3((unsigned)(n_heads * a.nseg)), dim3(kSumThreads), 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    if (a.nseg > 1) {
+        segment_sum_kernel<<<dim3((kD * kD + kD + 255) / 256, (unsigned)n_heads), dim3(256), 0, stream>>>(a);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t bph = (a.T + kNcBlockTokens - 1) / kNcBlockTokens;
+    noncausal_readout_kernel<FM><<<dim3((unsigned)(n_heads * bph)), dim3(kNcThreads), 0, stream>>>(a, (int)bph);
     return hipGetLastError();
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Segments per sequence: enough (sequence, segment) workgroups to give every compute
+// unit work, each segment a whole number of chunks and long enough to hold its slot in
+// Y, every segment (the last may be up to twice as long) below 2^31 bytes of Q so that
+// buffer offsets stay 32-bit.  Returns 0 when the grid would not fit.
+int64_t choose_segments(int64_t T, int64_t n_heads, int C, int64_t target)
+{
+    int64_t nseg = (target + n_heads - 1) / n_heads;
+    const int64_t min_len = ((kMinSegTokens + C - 1) / C) * C;
+    if (nseg > T / min_len)
+        nseg = T / min_len;
+    const int64_t max_len = ((int64_t)1 << 31) / (kD * 2) / 2;
+    if (nseg < (T + max_len - 1) / max_len)
+        nseg = (T + max_len - 1) / max_len;
+    if (nseg < 1)
+        nseg = 1;
+    if (n_heads * nseg > INT32_MAX)
+        return 0;
+    return nseg;
+}
 
 }  // namespace
 
 bool mfma_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk)
 {
     return io_dtype == LA_BF16 && d == kD && dv == kD && (chunk == 64 || chunk == 128);
+}
+
+bool mfma_noncausal_supported(la_dtype io_dtype, int32_t d, int32_t dv)
+{
+    return io_dtype == LA_BF16 && d == kD && dv == kD;
+}
+
+hipError_t launch_noncausal_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
+{
+    if (!aligned16(pa.Q) || !aligned16(pa.K) || !aligned16(pa.V) || !aligned16(pa.Y) || !aligned16(pa.S) ||
+        !aligned16(pa.z))
+        return launch_noncausal_general(pa, LA_BF16, stream);
+    Args a;
+    a.Q = static_cast<const bf16 *>(pa.Q);
+    a.K = static_cast<const bf16 *>(pa.K);
+    a.V = static_cast<const bf16 *>(pa.V);
+    a.alpha = nullptr;
+    a.Y = static_cast<bf16 *>(pa.Y);
+    a.S = static_cast<float *>(pa.S);
+    a.z = static_cast<float *>(pa.z);
+    a.T = pa.T;
+    a.eps = (float)pa.eps;
+    const int64_t nseg = choose_segments(pa.T, pa.n_heads, kPcC, LA_SEGMENT_TARGET_C64);
+    const int64_t bph = (pa.T + kNcBlockTokens - 1) / kNcBlockTokens;
+    if (nseg == 0 || pa.n_heads * bph > INT32_MAX)
+        return hipErrorInvalidValue;
+    a.nseg = (int)nseg;
+    a.seg_len = nseg == 1 ? pa.T : ((pa.T / nseg) / kPcC) * kPcC;  // the last segment takes the rest
+    return dispatch_feature_map(pa.phi, [&](auto fm) { return launch_nc<decltype(fm)::value>(a, pa.n_heads, stream); });
 }
 
 hipError_t launch_prefill_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
@@ -1307,30 +1588,23 @@ hipError_t launch_prefill_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
     a.T = pa.T;
     a.eps = (float)pa.eps;
 
-    // Segments: enough (sequence, segment) workgroups to give every compute unit
-    // work (two resident workgroups per unit at chunk 64, one at chunk 128), each
-    // segment a whole number of chunks and long enough to hold its slot in Y.
+    // one or two resident workgroups per compute unit at chunk 64, one at chunk 128
     const int C = pa.chunk;
-    const int64_t target = C == 64 ? LA_SEGMENT_TARGET_C64 : LA_SEGMENT_TARGET_C128;
-    int64_t nseg = (target + pa.n_heads - 1) / pa.n_heads;
-    const int64_t min_len = ((kMinSegTokens + C - 1) / C) * C;
-    if (nseg > pa.T / min_len)
-        nseg = pa.T / min_len;
-    // buffer offsets are 32-bit: keep every segment (the last may be up to twice as
-    // long) below 2^31 bytes of Q
-    const int64_t max_len = ((int64_t)1 << 31) / (kD * 2) / 2;
-    if (nseg < (pa.T + max_len - 1) / max_len)
-        nseg = (pa.T + max_len - 1) / max_len;
-    if (nseg < 1)
-        nseg = 1;
-    if (pa.n_heads * nseg > INT32_MAX)
+    const int64_t nseg =
+        choose_segments(pa.T, pa.n_heads, C, C == 64 ? LA_SEGMENT_TARGET_C64 : LA_SEGMENT_TARGET_C128);
+    if (nseg == 0)
         return hipErrorInvalidValue;
     a.nseg = (int)nseg;
     a.seg_len = nseg == 1 ? pa.T : ((pa.T / nseg) / C) * C;  // the last segment takes the rest
 
-    if (C == 64)
-        return pa.alpha ? launch_c<64, true>(a, pa.n_heads, stream) : launch_c<64, false>(a, pa.n_heads, stream);
-    return pa.alpha ? launch_c<128, true>(a, pa.n_heads, stream) : launch_c<128, false>(a, pa.n_heads, stream);
+    return dispatch_feature_map(pa.phi, [&](auto fm) {
+        constexpr int FM = decltype(fm)::value;
+        if (C == 64)
+            return pa.alpha ? launch_c<64, true, FM>(a, pa.n_heads, stream)
+                            : launch_c<64, false, FM>(a, pa.n_heads, stream);
+        return pa.alpha ? launch_c<128, true, FM>(a, pa.n_heads, stream)
+                        : launch_c<128, false, FM>(a, pa.n_heads, stream);
+    });
 }
 
 }  // namespace la

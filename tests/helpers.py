@@ -52,12 +52,19 @@ def max_abs(got, ref) -> float:
     return float(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64)).max())
 
 
-def oracle_prefill(Q, K, V, alpha, eps, S0=None, z0=None, threads=8):
+def oracle_prefill(Q, K, V, alpha, eps, S0=None, z0=None, threads=8, phi_mode="elu1"):
     """Oracle on the exact values of device tensors Q, K, V [B,H,T,d] etc."""
     return oracle.recurrence_heads(to_f64(Q), to_f64(K), to_f64(V),
                                    None if alpha is None else to_f64(alpha), eps=eps,
                                    S0=None if S0 is None else to_f64(S0),
-                                   z0=None if z0 is None else to_f64(z0), threads=threads)
+                                   z0=None if z0 is None else to_f64(z0), phi_mode=phi_mode, threads=threads)
+
+
+def oracle_noncausal(Q, K, V, eps, S0=None, z0=None, threads=8, phi_mode="elu1"):
+    """Non-causal oracle on the exact values of device tensors."""
+    return oracle.noncausal_heads(to_f64(Q), to_f64(K), to_f64(V), eps=eps,
+                                  S0=None if S0 is None else to_f64(S0),
+                                  z0=None if z0 is None else to_f64(z0), phi_mode=phi_mode, threads=threads)
 
 
 def assert_prefill_parity(Y, S, z, ref, bar: str, label: str = ""):

@@ -13,7 +13,7 @@ import recurrent_state_chunkwise_amd as la
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "linattn.h")
 
-OK, NULL, SHAPE, DTYPE, EPS, CHUNK, UNSUP, LAUNCH, ALIAS = range(9)
+OK, NULL, SHAPE, DTYPE, EPS, CHUNK, UNSUP, LAUNCH, ALIAS, PHI = range(10)
 F64, F32, BF16 = la.LA_F64, la.LA_F32, la.LA_BF16
 
 
@@ -34,13 +34,14 @@ def _declared_functions():
 def test_header_symbols_exported(lib):
     names = _declared_functions()
     assert set(names) >= {"la_state_init", "la_prefill_chunked", "la_decode_step", "la_delta_decode_step",
-                          "la_status_str", "la_prefill_variant"}
+                          "la_status_str", "la_prefill_variant", "la_prefill_chunked_fm", "la_decode_step_fm",
+                          "la_prefill_noncausal"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         s = la.la_status_str(code)
         assert isinstance(s, str) and s
     assert la.la_status_str(0) == "ok"
@@ -160,3 +161,69 @@ def test_binding_shape_contract_cpu():
     with pytest.raises(ValueError):
         la.la_delta_decode_step(torch.zeros(2, 3), torch.zeros(2, 3), torch.zeros(2, 1), None,
                                 torch.zeros(2, 1), torch.zeros(2, 3, 1))
+
+
+def prefill_fm(lib, phi=0, **kw):
+    a = dict(Q=P[0], K=P[1], V=P[2], alpha=None, io=BF16, B=1, H=1, T=8, d=4, dv=4, eps=1e-6, chunk=4, Y=P[3],
+             S=P[4], z=P[5], st=F32)
+    a.update(kw)
+    return lib.la_prefill_chunked_fm(a["Q"], a["K"], a["V"], a["alpha"], a["io"], a["B"], a["H"], a["T"], a["d"],
+                                     a["dv"], a["eps"], a["chunk"], a["Y"], a["S"], a["z"], a["st"], phi, None)
+
+
+def decode_fm(lib, phi=0, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], alpha=None, io=BF16, N=4, d=4, dv=4, eps=1e-6, y=P[3], S=P[4], z=P[5], st=F32)
+    a.update(kw)
+    return lib.la_decode_step_fm(a["q"], a["k"], a["v"], a["alpha"], a["io"], a["N"], a["d"], a["dv"], a["eps"],
+                                 a["y"], a["S"], a["z"], a["st"], phi, None)
+
+
+def noncausal(lib, Q=P[0], K=P[1], V=P[2], io=BF16, B=1, H=1, T=8, d=4, dv=4, eps=1e-6, Y=P[3], S=P[4], z=P[5],
+              st=F32, phi=0):
+    return lib.la_prefill_noncausal(Q, K, V, io, B, H, T, d, dv, eps, Y, S, z, st, phi, None)
+
+
+def test_feature_map_rejections(lib):
+    # an unknown map is LA_ERR_PHI; the other checks are those of the calls without _fm
+    for bad in (-1, 4, 99):
+        assert prefill_fm(lib, phi=bad) == PHI
+        assert decode_fm(lib, phi=bad) == PHI
+        assert noncausal(lib, phi=bad) == PHI
+    assert prefill_fm(lib, phi=1, Q=None) == NULL
+    assert prefill_fm(lib, phi=2, T=0) == SHAPE
+    assert prefill_fm(lib, phi=3, chunk=0) == CHUNK
+    assert prefill_fm(lib, phi=3, Y=P[0]) == ALIAS
+    assert decode_fm(lib, phi=1, N=0) == SHAPE
+    assert decode_fm(lib, phi=2, eps=-1.0) == EPS
+    assert decode_fm(lib, phi=3, y=P[1]) == ALIAS
+
+
+def test_noncausal_rejections(lib):
+    assert noncausal(lib, Q=None) == NULL
+    assert noncausal(lib, z=None) == NULL
+    assert noncausal(lib, T=0) == SHAPE
+    assert noncausal(lib, B=0) == SHAPE
+    assert noncausal(lib, dv=0) == SHAPE
+    assert noncausal(lib, B=1 << 40, H=1 << 40) == SHAPE
+    assert noncausal(lib, io=7) == DTYPE
+    assert noncausal(lib, io=BF16, st=F64) == DTYPE
+    assert noncausal(lib, io=F64, st=F32) == DTYPE
+    assert noncausal(lib, eps=math.nan) == EPS
+    assert noncausal(lib, eps=-1e-3) == EPS
+    assert noncausal(lib, d=129) == UNSUP
+    assert noncausal(lib, Y=P[2]) == ALIAS
+    assert noncausal(lib, S=ctypes.c_void_p(P[0].value + 16)) == ALIAS
+    assert noncausal(lib, z=P[4]) == ALIAS
+
+
+def test_binding_feature_map_names():
+    """Names map to the header's codes; an unknown name is a ValueError before any call."""
+    import torch
+    assert la.FEATURE_MAPS == {"elu1": 0, "relu1": 1, "relu_eps": 2, "sigmoid_eps": 3}
+    q = torch.zeros(1, 1, 2, 2)
+    with pytest.raises(ValueError):
+        la.la_prefill_noncausal(q, q, torch.zeros(1, 1, 2, 1), 1e-6, torch.zeros(1, 1, 2, 1),
+                                torch.zeros(1, 1, 2, 1), torch.zeros(1, 1, 2), phi="softplus")
+    with pytest.raises(ValueError):
+        la.la_prefill_noncausal(q, torch.zeros(1, 1, 2, 3), torch.zeros(1, 1, 2, 1), 1e-6, torch.zeros(1, 1, 2, 1),
+                                torch.zeros(1, 1, 2, 1), torch.zeros(1, 1, 2))

@@ -1,0 +1,237 @@
+"""GPU parity of the feature-map variants and of the non-causal form against the
+FP64 oracle, through the C ABI.
+
+Feature maps relu+1, relu+1e-5 and sigmoid+1e-5 (and ELU+1) on the causal MFMA prefill
+(chunk 64 and 128, gated and ungated), the general prefill (f32, f64), the decode step
+(bf16 at width 128, f32 general) and the non-causal form: the bf16 MFMA path with one
+and several segments, ragged lengths (below one 16-token tile, across read-out blocks),
+a carried incoming state, and the general path in f32, f64 and bf16 at other widths;
+plus the non-causal form at the B=4, H=16, T=4096 shape on sampled heads."""
+import math
+
+import numpy as np
+import pytest
+
+import recurrent_state_chunkwise_amd as la
+
+from helpers import (BF16_STATE_REL, BF16_Y_ABS, F32_REL, Z_SUM_REL, elem_rel, max_abs, maxnorm_rel,
+                     oracle_noncausal, oracle_prefill, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+MAPS = ["elu1", "relu1", "relu_eps", "sigmoid_eps"]
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    assert _t.cuda.is_available(), "GPU tests need a HIP device"
+    la.library()
+    return _t
+
+
+def _inputs(torch, B, H, T, d, dv, dtype, seed, gated=False, with_state=False, scale=None):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    sc = (1 / math.sqrt(128)) if scale is None else scale
+    sdt = torch.float64 if dtype == torch.float64 else torch.float32
+    mk = lambda w: (torch.randn((B, H, T, w), generator=g, device="cuda", dtype=sdt) * sc).to(dtype)
+    Q, K, V = mk(d), mk(d), mk(dv)
+    alpha = torch.sigmoid(torch.randn((B, H, T), generator=g, device="cuda", dtype=sdt) + 3.0) if gated else None
+    S0 = z0 = None
+    if with_state:
+        S0 = torch.randn((B, H, d, dv), generator=g, device="cuda", dtype=sdt) * 0.05
+        z0 = torch.rand((B, H, d), generator=g, device="cuda", dtype=sdt) * 20.0 + 1.0
+    return Q, K, V, alpha, S0, z0
+
+
+def _state(torch, B, H, d, dv, sdt, S0, z0):
+    S = torch.empty((B, H, d, dv), device="cuda", dtype=sdt)
+    z = torch.empty((B, H, d), device="cuda", dtype=sdt)
+    if S0 is None:
+        la.la_state_init(S, z)
+    else:
+        S.copy_(S0)
+        z.copy_(z0)
+    return S, z
+
+
+def _compare(Y, S, z, ref, bar, label):
+    Yr, Sr, zr, _ = ref
+    Yg, Sg, zg = to_f64(Y), to_f64(S), to_f64(z)
+    assert np.isfinite(Yg).all() and np.isfinite(Sg).all() and np.isfinite(zg).all(), label
+    ya, yr = max_abs(Yg, Yr), maxnorm_rel(Yg, Yr, 2)
+    sr, zrel = maxnorm_rel(Sg, Sr, 2), elem_rel(zg, zr)
+    print("%s: y abs %.2e y rel %.2e S rel %.2e z rel %.2e" % (label, ya, yr, sr, zrel))
+    if bar == "bf16":
+        assert ya <= BF16_Y_ABS and sr <= BF16_STATE_REL and zrel <= BF16_STATE_REL, (label, ya, sr, zrel)
+        # tighter expectation from bf16 operand rounding (the operands are rounded once)
+        assert yr <= 2e-2 and sr <= 5e-3 and zrel <= Z_SUM_REL, (label, yr, sr, zrel)
+    elif bar == "f32":
+        assert yr <= F32_REL and sr <= F32_REL and zrel <= F32_REL, (label, yr, sr, zrel)
+    else:
+        assert yr <= 1e-11 and sr <= 1e-11 and zrel <= 1e-11, (label, yr, sr, zrel)
+
+
+# ---------------------------------------------------------------- causal prefill, every map
+CAUSAL = [
+    # B, H, T, d, dv, dtype, chunk, gated, with_state
+    (1, 3, 200, 128, 128, "bf16", 64, False, True),
+    (1, 2, 333, 128, 128, "bf16", 64, True, False),
+    (1, 2, 300, 128, 128, "bf16", 128, True, True),
+    (1, 1, 700, 128, 128, "bf16", 64, False, False),   # several segments
+    (2, 2, 77, 16, 24, "f32", 16, True, True),
+    (1, 2, 50, 8, 8, "f64", 7, False, True),
+]
+
+
+@pytest.mark.parametrize("phi", MAPS)
+@pytest.mark.parametrize("case", CAUSAL, ids=lambda c: "B%dH%dT%d_d%d_%s_c%d%s%s" % (
+    c[0], c[1], c[2], c[3], c[5], c[6], "_g" if c[7] else "", "_s" if c[8] else ""))
+def test_causal_prefill_feature_maps(torch, phi, case):
+    B, H, T, d, dv, dt, chunk, gated, with_state = case
+    dtype = {"bf16": torch.bfloat16, "f32": torch.float32, "f64": torch.float64}[dt]
+    sdt = torch.float64 if dt == "f64" else torch.float32
+    seed = 100 + MAPS.index(phi) * 10 + CAUSAL.index(case)
+    Q, K, V, alpha, S0, z0 = _inputs(torch, B, H, T, d, dv, dtype, seed, gated, with_state,
+                                     scale=None if dt == "bf16" else 1.0)
+    S, z = _state(torch, B, H, d, dv, sdt, S0, z0)
+    Y = torch.empty_like(V)
+    la.la_prefill_chunked_fm(Q, K, V, alpha, 1e-6, chunk, Y, S, z, phi=phi)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(Q, K, V, alpha, 1e-6, S0, z0, phi_mode=phi)
+    _compare(Y, S, z, ref, dt, "causal %s %s" % (phi, case))
+
+
+def test_elu1_fm_matches_plain_call_bitwise(torch):
+    Q, K, V, alpha, S0, z0 = _inputs(torch, 1, 2, 300, 128, 128, torch.bfloat16, 7, gated=True, with_state=True)
+    outs = []
+    for fm in (False, True):
+        S, z = _state(torch, 1, 2, 128, 128, torch.float32, S0, z0)
+        Y = torch.empty_like(V)
+        if fm:
+            la.la_prefill_chunked_fm(Q, K, V, alpha, 1e-6, 64, Y, S, z, phi="elu1")
+        else:
+            la.la_prefill_chunked(Q, K, V, alpha, 1e-6, 64, Y, S, z)
+        torch.cuda.synchronize()
+        outs.append((Y.clone(), S.clone(), z.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- decode, every map
+@pytest.mark.parametrize("phi", MAPS)
+@pytest.mark.parametrize("width,dt", [(128, "bf16"), (40, "f32")])
+def test_decode_feature_maps(torch, phi, width, dt):
+    N, steps = 96, 3
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(300 + MAPS.index(phi))
+    sc = 1 / math.sqrt(128) if dt == "bf16" else 1.0
+    q = (torch.randn((steps, N, width), generator=g, device="cuda") * sc).to(dtype)
+    k = (torch.randn((steps, N, width), generator=g, device="cuda") * sc).to(dtype)
+    v = (torch.randn((steps, N, width), generator=g, device="cuda") * sc).to(dtype)
+    alpha = torch.sigmoid(torch.randn((steps, N), generator=g, device="cuda") + 2.0)
+    S = torch.randn((N, width, width), generator=g, device="cuda") * 0.05
+    z = torch.rand((N, width), generator=g, device="cuda") * 5.0 + 1.0
+    S0, z0 = S.clone(), z.clone()
+    ys = []
+    for t in range(steps):
+        y = torch.empty((N, width), device="cuda", dtype=dtype)
+        la.la_decode_step_fm(q[t].contiguous(), k[t].contiguous(), v[t].contiguous(),
+                             alpha[t].contiguous() if t % 2 else None, 1e-6, y, S, z, phi=phi)
+        ys.append(y)
+    torch.cuda.synchronize()
+    Yg = np.stack([to_f64(y) for y in ys], axis=1)  # [N, steps, dv]
+    a = to_f64(alpha).T.copy()
+    a[:, 0::2] = 1.0  # even steps ran ungated
+    import oracle
+    Yr, Sr, zr, _ = oracle.recurrence_heads(to_f64(q).transpose(1, 0, 2), to_f64(k).transpose(1, 0, 2),
+                                            to_f64(v).transpose(1, 0, 2), a, eps=1e-6, S0=to_f64(S0), z0=to_f64(z0),
+                                            phi_mode=phi, threads=8)
+    # decode arithmetic is fp32 throughout: the fp32 bar for S and z; y is rounded to the io dtype
+    sr, zrel = maxnorm_rel(to_f64(S), Sr, 2), elem_rel(to_f64(z), zr)
+    yr = maxnorm_rel(Yg, Yr, 2)
+    print("decode %s %s: y rel %.2e S rel %.2e z rel %.2e" % (phi, dt, yr, sr, zrel))
+    assert sr <= F32_REL and zrel <= F32_REL
+    assert yr <= (2 ** -8 if dt == "bf16" else F32_REL)
+
+
+# ---------------------------------------------------------------- non-causal form
+NONCAUSAL = [
+    # B, H, T, d, dv, dtype, with_state
+    (1, 1, 1, 128, 128, "bf16", False),
+    (2, 3, 15, 128, 128, "bf16", True),        # below one 16-token tile
+    (1, 4, 259, 128, 128, "bf16", False),      # one segment, ragged
+    (1, 2, 700, 128, 128, "bf16", True),       # two segments, ragged last one
+    (1, 1, 2000, 128, 128, "bf16", False),     # six segments, two read-out blocks
+    (1, 1, 1041, 128, 128, "bf16", True),      # read-out block boundary + ragged tile
+    (2, 2, 90, 16, 24, "f32", True),
+    (1, 2, 40, 8, 12, "f64", True),
+    (1, 2, 100, 64, 128, "bf16", False),       # bf16 at another width: general kernel
+]
+
+
+def _nc_id(c):
+    return "B%dH%dT%d_d%ddv%d_%s%s" % (c[0], c[1], c[2], c[3], c[4], c[5], "_s" if c[6] else "")
+
+
+@pytest.mark.parametrize("phi", MAPS)
+@pytest.mark.parametrize("case", NONCAUSAL, ids=_nc_id)
+def test_noncausal(torch, phi, case):
+    B, H, T, d, dv, dt, with_state = case
+    dtype = {"bf16": torch.bfloat16, "f32": torch.float32, "f64": torch.float64}[dt]
+    sdt = torch.float64 if dt == "f64" else torch.float32
+    seed = 500 + MAPS.index(phi) * 20 + NONCAUSAL.index(case)
+    Q, K, V, _, S0, z0 = _inputs(torch, B, H, T, d, dv, dtype, seed, with_state=with_state,
+                                 scale=None if dt == "bf16" else 1.0)
+    S, z = _state(torch, B, H, d, dv, sdt, S0, z0)
+    Y = torch.empty_like(V)
+    la.la_prefill_noncausal(Q, K, V, 1e-6, Y, S, z, phi=phi)
+    torch.cuda.synchronize()
+    ref = oracle_noncausal(Q, K, V, 1e-6, S0, z0, phi_mode=phi)
+    _compare(Y, S, z, ref, dt, "noncausal %s %s" % (phi, _nc_id(case)))
+
+
+def test_noncausal_page_example_at_width_128(torch):
+    """Exercise 1 of the hs-black page embedded at width 128 (phi(-inf) = 0 pads the
+    features, phi(0) = 1, phi(1) = 2): every token reads the final state, whose output
+    the page prints as [17/6, 11/6]; exact in bf16 up to the output rounding."""
+    T = 3
+    ninf = -math.inf
+    Q = torch.full((1, 1, T, 128), ninf)
+    K = torch.full((1, 1, T, 128), ninf)
+    V = torch.zeros((1, 1, T, 128))
+    for t in range(T):
+        Q[0, 0, t, 0], Q[0, 0, t, 1] = 1.0, 0.0     # q~ = [2, 1]
+    K[0, 0, 0, 0] = 0.0                              # k~1 = [1, 0]
+    K[0, 0, 1, 1] = 0.0                              # k~2 = [0, 1]
+    K[0, 0, 2, 0], K[0, 0, 2, 1] = 0.0, 0.0          # k~3 = [1, 1]
+    V[0, 0, :, :2] = torch.tensor([[2.0, 1.0], [4.0, 3.0], [3.0, 2.0]])
+    Qd, Kd, Vd = (x.to("cuda", torch.bfloat16) for x in (Q, K, V))
+    S, z = _state(torch, 1, 1, 128, 128, torch.float32, None, None)
+    Y = torch.empty_like(Vd)
+    la.la_prefill_noncausal(Qd, Kd, Vd, 0.0, Y, S, z, phi="elu1")
+    torch.cuda.synchronize()
+    want = torch.tensor([17 / 6, 11 / 6]).to(torch.bfloat16).to(torch.float64).numpy()
+    Yg = to_f64(Y)[0, 0]
+    assert np.array_equal(Yg[:, :2], np.tile(want, (T, 1)))
+    assert np.all(Yg[:, 2:] == 0.0)
+    assert np.array_equal(to_f64(S)[0, 0, :2, :2], [[5.0, 3.0], [7.0, 5.0]])
+    assert np.array_equal(to_f64(z)[0, 0, :2], [2.0, 2.0]) and np.all(to_f64(z)[0, 0, 2:] == 0.0)
+
+
+def test_noncausal_full_shape_sampled(torch):
+    """B=4, H=16, T=4096 at d = dv = 128 (the ungated prefill shape), in the launch
+    configuration timed by the benchmark; the oracle runs on 3 sampled heads (whole
+    sequences: the non-causal output of a head depends on all of it)."""
+    B, H, T = 4, 16, 4096
+    Q, K, V, _, _, _ = _inputs(torch, B, H, T, 128, 128, torch.bfloat16, 77)
+    S, z = _state(torch, B, H, 128, 128, torch.float32, None, None)
+    Y = torch.empty_like(V)
+    la.la_prefill_noncausal(Q, K, V, 1e-6, Y, S, z)
+    torch.cuda.synchronize()
+    for (b, h) in ((0, 0), (2, 7), (3, 15)):
+        ref = oracle_noncausal(Q[b:b + 1, h:h + 1], K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], 1e-6)
+        _compare(Y[b:b + 1, h:h + 1], S[b:b + 1, h:h + 1], z[b:b + 1, h:h + 1], ref, "bf16",
+                 "noncausal full shape head (%d, %d)" % (b, h))
