@@ -30,6 +30,9 @@ Source of truth is the page "Linear attention：把历史写进状态"
   (ai-master.cc): all keys and values are written into the state first, then
   every query reads the full state (eps added to the denominator), in C;
   :func:`quadratic_unmasked` is its brute-force unmasked counterpart.
+* :func:`softmax_decode` -- the softmax attention row y = sum softmax(q.k_i/sqrt(d)) v_i
+  of section "先看普通 attention 在读什么" (hs-black page), the explicit-history
+  comparator of the datawhalechina chapter's Step 5, in C.
 
 Feature maps (``phi_mode``): ``"elu1"`` (ELU+1, the default), ``"relu1"``
 (max(x,0)+1, the positive map of the datawhalechina chapter "Linear Attention and
@@ -102,6 +105,9 @@ def _load():
             lib.oracle_noncausal.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                              dp, dp, dp, ctypes.c_double, ctypes.c_int32,
                                              dp, dp, dp, dp]
+            lib.oracle_softmax_decode.restype = ctypes.c_int
+            lib.oracle_softmax_decode.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, dp, dp, dp,
+                                                  ctypes.c_double, dp, dp]
             lib.oracle_delta_steps.restype = ctypes.c_int
             lib.oracle_delta_steps.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                dp, dp, dp, dp, dp, dp, dp]
@@ -474,3 +480,44 @@ def quadratic_unmasked(q, k, v, eps: float = 1e-6, S0=None, z0=None, phi_mode: s
     if z0 is not None:
         den = den + qf @ _f64(z0)
     return num / (den + eps)[:, None], den
+
+
+def softmax_decode(q, K, V, scale=None):
+    """Softmax attention of one query over an explicit history: y = sum_i w_i v_i with
+    w = softmax(scale * K q) (scale defaults to 1/sqrt(r)).
+
+    q: [r]; K: [L, r]; V: [L, dv].  Returns ``(y [dv], w [L])``.
+    """
+    q, K, V = _f64(q).reshape(-1), _f64(K), _f64(V)
+    if K.ndim != 2 or V.ndim != 2 or K.shape[0] != V.shape[0] or K.shape[1] != q.shape[0] or K.shape[0] == 0:
+        raise ValueError("q must be [r], K [L, r] and V [L, dv] with L >= 1")
+    L, r = K.shape
+    dv = V.shape[1]
+    if r == 0 or dv == 0:
+        raise ValueError("feature and value widths must be >= 1")
+    sc = 1.0 / np.sqrt(r) if scale is None else float(scale)
+    y = np.empty(dv)
+    w = np.empty(L)
+    rc = _load().oracle_softmax_decode(L, r, dv, _ptr(q), _ptr(K), _ptr(V), sc, _ptr(y), _ptr(w))
+    if rc != 0:
+        raise RuntimeError("oracle_softmax_decode rejected its arguments")
+    return y, w
+
+
+def softmax_decode_heads(q, K, V, scale=None, threads: int = 1):
+    """:func:`softmax_decode` over independent heads: q [n, r]; K [n, L, r]; V [n, L, dv].
+    Returns ``y [n, dv]``."""
+    q, K, V = _f64(q), _f64(K), _f64(V)
+    n = q.shape[0]
+    Y = np.empty((n, V.shape[-1]))
+
+    def one(h):
+        Y[h] = softmax_decode(q[h], K[h], V[h], scale)[0]
+
+    if threads <= 1 or n == 1:
+        for h in range(n):
+            one(h)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(n)))
+    return Y

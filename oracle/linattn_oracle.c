@@ -240,3 +240,49 @@ int oracle_delta_steps(int64_t T, int32_t r, int32_t dv,
     free(e);
     return 0;
 }
+
+/*
+ * Softmax attention decode, the comparator of the datawhalechina chapter "Linear
+ * Attention and Recurrent State" (Step 5: an explicit K/V history against the fixed
+ * recurrent state).  The row it computes is the one of the hs-black.github.io page,
+ * section "先看普通 attention 在读什么": the query scores every history key, the scores
+ * are normalised by softmax, and the values are summed with those weights:
+ *   s_i = scale * (q . k_i),   w_i = exp(s_i - max_j s_j),   y = sum_i w_i v_i / sum_i w_i
+ * for i = 0 .. L-1 (subtracting the maximum leaves the weights unchanged and keeps exp
+ * finite).  One head: q [r]; K [L, r]; V [L, dv]; y [dv] out; w [L] or NULL (out: the
+ * normalised weights).  Returns 0, or -1 on a bad argument.
+ */
+int oracle_softmax_decode(int64_t L, int32_t r, int32_t dv, const double *q, const double *K,
+                          const double *V, double scale, double *y, double *w)
+{
+    if (L < 1 || r < 1 || dv < 1 || !q || !K || !V || !y)
+        return -1;
+    double *s = (double *)malloc(sizeof(double) * (size_t)L);
+    if (!s)
+        return -1;
+    double mx = -INFINITY;
+    for (int64_t i = 0; i < L; ++i) {
+        double acc = 0.0;
+        for (int32_t c = 0; c < r; ++c)
+            acc += q[c] * K[i * r + c];
+        s[i] = scale * acc;
+        if (s[i] > mx)
+            mx = s[i];
+    }
+    double sum = 0.0;
+    for (int64_t i = 0; i < L; ++i) {
+        s[i] = exp(s[i] - mx);
+        sum += s[i];
+    }
+    for (int32_t j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < L; ++i)
+            acc += s[i] * V[i * dv + j];
+        y[j] = acc / sum;
+    }
+    if (w)
+        for (int64_t i = 0; i < L; ++i)
+            w[i] = s[i] / sum;
+    free(s);
+    return 0;
+}
