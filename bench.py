@@ -14,11 +14,14 @@ line also carries:
                 (133,120 B per state-step);
   noncausal     la_prefill_noncausal on the ungated prefill shape (every query reads
                 the state of the whole sequence), timed the same way, same roofline bytes;
+  kv_vs_state   an explicit K/V history (softmax decode over L rows) against the fixed
+                recurrent state (one decode step), 8 heads x 64, bf16, L = 512, 2048,
+                8192: state bytes, step time, peak memory; also at 128 sequences;
   other         the gated prefill workloads, timed the same way;
   cpu_baseline  the FP64 oracle timed on this host's cores on a sample of the
                 prefill workload.
 Run: python bench.py [--gpus 1] [--steps K] [--warmup W]
-     python bench.py --only prefill|noncausal|decode|delta|copy   (one workload, for profiler runs; `copy`
+     python bench.py --only prefill|noncausal|decode|delta|kvstate|copy   (one workload, for profiler runs; `copy`
      is a plain 1 GiB device-to-device copy used to calibrate the HBM byte counters)
 """
 from __future__ import annotations
@@ -190,6 +193,103 @@ def time_delta(torch, la, wl, cfg, warmup=10, steps=None):
     return total_ms, call_ms
 
 
+def time_kv_state(torch, la, wl, cfg):
+    """The history path and the state path at each length L, P1's protocol: `warmup` steps,
+    then `repeats` steps bracketed by events, mean per step.  Memory: what each path holds
+    during its steps (peak over the timed loop) and, for the state path, the peak of
+    building the state from the same L-1 earlier rows (a prefill whose outputs are
+    discarded)."""
+    H, d = cfg.n_heads, cfg.d
+    bf16 = torch.bfloat16
+    rows = []
+
+    def timed(step_fn, steps):
+        """(eager ms, graph ms) per step: P1's protocol with the steps launched one by one
+        from Python (at these sizes the launch rate can set the pace), then the same
+        `repeats` steps captured once into a HIP graph and replayed (device time)."""
+        for i in range(cfg.warmup):
+            step_fn(*steps[i])
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(cfg.repeats):
+            step_fn(*steps[cfg.warmup + i])
+        t1.record()
+        torch.cuda.synchronize()
+        eager = t0.elapsed_time(t1) / cfg.repeats
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(cfg.repeats):
+                step_fn(*steps[cfg.warmup + i])
+        graph.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        replay = t0.elapsed_time(t1) / cfg.repeats
+        del graph
+        return eager, replay
+
+    for L in cfg.lengths:
+        hk, hv = wl.kv_state_history(cfg, L, "cuda")
+        steps = wl.kv_state_steps(cfg, L, cfg.warmup + cfg.repeats, "cuda")
+        # explicit history: caches of L rows, the step writes row L-1 and attends over all
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        Kc = torch.empty((H, L, d), device="cuda", dtype=bf16)
+        Vc = torch.empty((H, L, d), device="cuda", dtype=bf16)
+        Kc[:, :L - 1].copy_(hk)
+        Vc[:, :L - 1].copy_(hv)
+        y = torch.empty((H, d), device="cuda", dtype=bf16)
+        need = la.la_softmax_decode_workspace_bytes(la.LA_BF16, H, L, d)
+        ws = torch.empty(max(need, 1), device="cuda", dtype=torch.uint8)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        hist_ms, hist_graph_ms = timed(
+            lambda q, k, v: la.la_softmax_decode_step(q, k, v, L - 1, Kc, Vc, y, workspace=ws), steps)
+        hist_peak = torch.cuda.max_memory_allocated() - base
+        hist_finite = bool(torch.isfinite(y.float()).all())
+        del Kc, Vc, ws, y
+        # fixed state: S, z built from the same L-1 rows, then one decode step per call
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        S = torch.empty((H, 1, d, d), device="cuda")
+        z = torch.empty((H, 1, d), device="cuda")
+        la.la_state_init(S, z)
+        Yseed = torch.empty((H, 1, L - 1, d), device="cuda", dtype=bf16)
+        hk4, hv4 = hk.view(H, 1, L - 1, d), hv.view(H, 1, L - 1, d)
+        la.la_prefill_chunked(hk4, hk4, hv4, None, cfg.eps, 64, Yseed, S, z)
+        torch.cuda.synchronize()
+        setup_peak = torch.cuda.max_memory_allocated() - base
+        del Yseed
+        S2, z2 = S.view(H, d, d), z.view(H, d)
+        y = torch.empty((H, d), device="cuda", dtype=bf16)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        state_ms, state_graph_ms = timed(lambda q, k, v: la.la_decode_step(q, k, v, None, cfg.eps, y, S2, z2), steps)
+        state_peak = torch.cuda.max_memory_allocated() - base
+        state_finite = bool(torch.isfinite(y.float()).all())
+        del S, z, S2, z2, y, hk, hv, hk4, hv4, steps
+        hist_bytes = 2 * H * L * d * 2
+        state_bytes = H * (d * d + d) * 4
+        rows.append({
+            "L": L, "history_bytes": hist_bytes, "state_bytes": state_bytes,
+            "history_step_ms": hist_ms, "state_step_ms": state_ms, "state_over_history_time": state_ms / hist_ms,
+            "history_step_ms_graph": hist_graph_ms, "state_step_ms_graph": state_graph_ms,
+            "state_over_history_time_graph": state_graph_ms / hist_graph_ms,
+            "history_peak_bytes": hist_peak, "state_peak_bytes": state_peak, "state_setup_peak_bytes": setup_peak,
+            "history_read_GBps_graph": hist_bytes / (hist_graph_ms / 1e3) / 1e9,
+            "finite": hist_finite and state_finite,
+        })
+    return {"workload": cfg.name, "heads": H, "d": d, "dtype": "bf16",
+            "protocol": "warmup %d, repeats %d, events around the repeats, mean per step; *_graph: the same "
+                        "repeats captured in one HIP graph and replayed" % (cfg.warmup, cfg.repeats),
+            "rows": rows}
+
+
 def cpu_baseline(wl, torch):
     """The FP64 oracle on this host's cores, on a sample of the prefill workload."""
     import oracle
@@ -221,7 +321,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the decode and gated workloads")
-    ap.add_argument("--only", choices=["prefill", "noncausal", "decode", "delta", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "noncausal", "decode", "delta", "kvstate", "copy"], default=None,
                     help="run one workload only and print its timing (for profiler runs)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="steps to time with --only decode or --only delta (default: the workload's)")
@@ -256,6 +356,10 @@ def main():
         steps = args.decode_steps or wl.DELTA_DECODE.steps
         d_total, d_call = time_delta(torch, la, wl, wl.DELTA_DECODE, steps=steps)
         print(json.dumps({"only": "delta", "steps": steps, "ms_per_step": d_total / steps, "call_ms": d_call}))
+        return
+    if args.only == "kvstate":
+        print(json.dumps({"only": "kvstate", "kv_vs_state": time_kv_state(torch, la, wl, wl.KV_STATE),
+                          "kv_vs_state_batched": time_kv_state(torch, la, wl, wl.KV_STATE_BATCHED)}))
         return
     cfg = wl.PREFILL_UNGATED
     if args.only == "noncausal":
@@ -345,6 +449,8 @@ def main():
                          "traffic": measured_traffic("noncausal"),
                          "call_ms": n_call, "algorithmic_bytes": nbytes},
         }
+        out["kv_vs_state"] = time_kv_state(torch, la, wl, wl.KV_STATE)
+        out["kv_vs_state_batched"] = time_kv_state(torch, la, wl, wl.KV_STATE_BATCHED)
         other = []
         for ocfg in (wl.PREFILL_GATED, wl.PREFILL_LONG):
             steps = 10 if ocfg.T <= 16384 else 3

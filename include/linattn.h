@@ -55,7 +55,9 @@ typedef enum la_status {
     LA_ERR_UNSUPPORTED = 6, /* valid request with no kernel: d or dv > 128, chunk > 128 */
     LA_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
     LA_ERR_ALIAS = 8,       /* an output overlaps an input or another output */
-    LA_ERR_PHI = 9          /* unknown feature map */
+    LA_ERR_PHI = 9,         /* unknown feature map */
+    LA_ERR_WORKSPACE = 10,  /* workspace missing or too small */
+    LA_ERR_SCALE = 11       /* scale is NaN or infinite */
 } la_status;
 
 typedef enum la_dtype {
@@ -210,6 +212,36 @@ la_status la_prefill_noncausal(const void *Q, const void *K, const void *V, la_d
                                int64_t B, int64_t H, int64_t T, int32_t d, int32_t dv,
                                double eps, void *Y, void *S, void *z, la_dtype state_dtype,
                                la_feature_map phi, hipStream_t stream);
+
+/*
+ * la_softmax_decode_step -- one decode step of softmax attention over an explicit K/V
+ * history, the comparator that the datawhalechina chapter "Linear Attention and
+ * Recurrent State" (Step 5) sets against the fixed recurrent state.  The row is the one
+ * of section "先看普通 attention 在读什么" of the hs-black.github.io page: every history key
+ * is scored against the query, the scores are normalised by softmax and the values are
+ * summed with those weights.  For each head h:
+ *   K_cache[h][pos] = k[h], V_cache[h][pos] = v[h]   (the new token joins the history)
+ *   y[h] = sum_{i=0..pos} w_i V_cache[h][i],  w = softmax_i(scale * q[h] . K_cache[h][i])
+ *   q, k      [n_heads, d]            io_dtype, read
+ *   v         [n_heads, dv]           io_dtype, read
+ *   K_cache   [n_heads, capacity, d]  io_dtype, rows 0..pos-1 read, row pos written
+ *   V_cache   [n_heads, capacity, dv] io_dtype, same
+ *   y         [n_heads, dv]           io_dtype, written
+ *   scale     any finite value (1/sqrt(d) for the page's row)
+ *   workspace device buffer of at least la_softmax_decode_workspace_bytes(io_dtype,
+ *             n_heads, pos + 1, dv) bytes (NULL allowed when that is 0), overwritten
+ * Arithmetic in fp32 (fp64 for f64 io).  Errors: LA_ERR_NULL, LA_ERR_SHAPE (sizes < 1,
+ * pos < 0 or pos >= capacity), LA_ERR_DTYPE, LA_ERR_UNSUPPORTED (d or dv > 128),
+ * LA_ERR_SCALE, LA_ERR_WORKSPACE, LA_ERR_ALIAS, LA_ERR_LAUNCH.
+ */
+la_status la_softmax_decode_step(const void *q, const void *k, const void *v, la_dtype io_dtype,
+                                 int64_t n_heads, int32_t d, int32_t dv, int64_t pos, int64_t capacity,
+                                 void *K_cache, void *V_cache, double scale, void *y,
+                                 void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes la_softmax_decode_step needs for a history of L rows (L = pos + 1);
+ * 0 when none is needed, -1 for invalid arguments. */
+int64_t la_softmax_decode_workspace_bytes(la_dtype io_dtype, int64_t n_heads, int64_t L, int32_t dv);
 
 /* Static description of a status code; never NULL. */
 const char *la_status_str(la_status status);

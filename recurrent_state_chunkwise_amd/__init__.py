@@ -22,7 +22,8 @@ __all__ = [
     "LA_F64", "LA_F32", "LA_BF16", "LA_PHI_ELU1", "LA_PHI_RELU1", "LA_PHI_RELU_EPS", "LA_PHI_SIGMOID_EPS",
     "FEATURE_MAPS", "LaArgumentError", "LaLaunchError",
     "la_state_init", "la_prefill_chunked", "la_prefill_chunked_fm", "la_prefill_noncausal", "la_decode_step",
-    "la_decode_step_fm", "la_delta_decode_step", "la_status_str", "la_prefill_variant", "library", "library_path",
+    "la_decode_step_fm", "la_delta_decode_step", "la_softmax_decode_step", "la_softmax_decode_workspace_bytes",
+    "la_status_str", "la_prefill_variant", "library", "library_path",
 ]
 
 LA_F64, LA_F32, LA_BF16 = 0, 1, 2
@@ -34,6 +35,7 @@ FEATURE_MAPS = {"elu1": LA_PHI_ELU1, "relu1": LA_PHI_RELU1, "relu_eps": LA_PHI_R
 STATUS = {
     0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_DTYPE", 4: "LA_ERR_EPS",
     5: "LA_ERR_CHUNK", 6: "LA_ERR_UNSUPPORTED", 7: "LA_ERR_LAUNCH", 8: "LA_ERR_ALIAS", 9: "LA_ERR_PHI",
+    10: "LA_ERR_WORKSPACE", 11: "LA_ERR_SCALE",
 }
 LA_ERR_LAUNCH = 7
 
@@ -96,6 +98,11 @@ def library() -> ctypes.CDLL:
             lib.la_prefill_noncausal.restype = ctypes.c_int
             lib.la_prefill_noncausal.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i32, i32, f64, vp, vp, vp,
                                                  ctypes.c_int, ctypes.c_int, vp]
+            lib.la_softmax_decode_step.restype = ctypes.c_int
+            lib.la_softmax_decode_step.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, i32, i64, i64, vp, vp, f64,
+                                                   vp, vp, i64, vp]
+            lib.la_softmax_decode_workspace_bytes.restype = i64
+            lib.la_softmax_decode_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
             lib.la_prefill_variant.restype = ctypes.c_int32
             lib.la_prefill_variant.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int]
             _lib = lib
@@ -317,6 +324,44 @@ def la_delta_decode_step(q, k, v, beta, y, S, stream=None) -> None:
     rc = library().la_delta_decode_step(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, N, d, dv, ptrs[4], ptrs[5], st,
                                         _stream_ptr(q, stream))
     _check(rc, "la_delta_decode_step")
+
+
+def la_softmax_decode_workspace_bytes(io_dtype: int, n_heads: int, L: int, dv: int) -> int:
+    """Workspace bytes of la_softmax_decode_step for a history of L rows (0: none needed)."""
+    return int(library().la_softmax_decode_workspace_bytes(int(io_dtype), int(n_heads), int(L), int(dv)))
+
+
+def la_softmax_decode_step(q, k, v, pos: int, K_cache, V_cache, y, scale=None, workspace=None,
+                           stream=None) -> None:
+    """Softmax attention decode over an explicit history: row `pos` of the caches takes
+    (k, v), then y = softmax(scale * K_cache[:pos+1] q) V_cache[:pos+1] per head.
+
+    q, k: [H, d]; v, y: [H, dv]; K_cache: [H, capacity, d]; V_cache: [H, capacity, dv];
+    scale defaults to 1/sqrt(d).  A workspace (uint8 device tensor) is allocated here
+    when the call needs one and none is given.
+    """
+    if q.dim() != 2 or tuple(k.shape) != tuple(q.shape):
+        raise ValueError("q and k must both be [H, d] with the same shape")
+    H, d = q.shape
+    if v.dim() != 2 or v.shape[0] != H or tuple(y.shape) != tuple(v.shape):
+        raise ValueError("v and y must be [H, dv] with q's H")
+    dv = v.shape[1]
+    if K_cache.dim() != 3 or tuple(K_cache.shape[::2]) != (H, d):
+        raise ValueError("K_cache must be [H, capacity, d]")
+    cap = K_cache.shape[1]
+    if tuple(V_cache.shape) != (H, cap, dv):
+        raise ValueError("V_cache must be [H, capacity, dv] with K_cache's capacity")
+    _same_dtype("q, k, v, y, K_cache, V_cache", (q, k, v, y, K_cache, V_cache))
+    io = _dtype_code(q)
+    sc = 1.0 / d ** 0.5 if scale is None else float(scale)
+    need = la_softmax_decode_workspace_bytes(io, H, int(pos) + 1, dv) if 0 <= int(pos) < cap else 0
+    if need > 0 and workspace is None:
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ptrs = _device_ptrs(q, k, v, K_cache, V_cache, y, workspace)
+    rc = library().la_softmax_decode_step(ptrs[0], ptrs[1], ptrs[2], io, H, d, dv, int(pos), cap, ptrs[3], ptrs[4],
+                                          sc, ptrs[5], ptrs[6], wbytes, _stream_ptr(q, stream))
+    _check(rc, "la_softmax_decode_step")
 
 
 def la_prefill_variant(io_dtype: int, d: int, dv: int, chunk: int, gated: bool, state_dtype: int) -> int:

@@ -118,6 +118,10 @@ const char *la_status_str(la_status s)
         return "an output buffer overlaps an input or another output";
     case LA_ERR_PHI:
         return "unknown feature map";
+    case LA_ERR_WORKSPACE:
+        return "workspace missing or smaller than la_softmax_decode_workspace_bytes";
+    case LA_ERR_SCALE:
+        return "scale must be finite";
     }
     return "unknown status";
 }
@@ -283,6 +287,53 @@ la_status la_delta_decode_step(const void *q, const void *k, const void *v, cons
     la::DeltaArgs a{q, k, v, beta, n_states, d, dv, y, S};
     (void)hipGetLastError();
     return launched(la::launch_delta_decode(a, io_dtype, stream));
+}
+
+int64_t la_softmax_decode_workspace_bytes(la_dtype io_dtype, int64_t n_heads, int64_t L, int32_t dv)
+{
+    if (!known_dtype(io_dtype) || n_heads < 1 || L < 1 || dv < 1 || dv > LA_MAX_WIDTH)
+        return -1;
+    const int64_t splits = la::softmax_decode_splits(L);
+    if (splits == 1)
+        return 0;
+    int64_t b;
+    if (!prod_ok({n_heads, splits, 2 + (int64_t)dv, io_dtype == LA_F64 ? 8 : 4}, &b))
+        return -1;
+    return b;
+}
+
+la_status la_softmax_decode_step(const void *q, const void *k, const void *v, la_dtype io_dtype, int64_t n_heads,
+                                 int32_t d, int32_t dv, int64_t pos, int64_t capacity, void *K_cache, void *V_cache,
+                                 double scale, void *y, void *workspace, int64_t workspace_bytes, hipStream_t stream)
+{
+    if (!q || !k || !v || !K_cache || !V_cache || !y)
+        return LA_ERR_NULL;
+    if (n_heads < 1 || d < 1 || dv < 1 || pos < 0 || capacity <= pos || n_heads > INT32_MAX)
+        return LA_ERR_SHAPE;
+    if (!known_dtype(io_dtype))
+        return LA_ERR_DTYPE;
+    if (d > LA_MAX_WIDTH || dv > LA_MAX_WIDTH)
+        return LA_ERR_UNSUPPORTED;
+    if (!isfinite(scale))
+        return LA_ERR_SCALE;
+    int64_t qk, vy, kc, vc;
+    const int64_t ei = dtype_bytes(io_dtype);
+    if (!prod_ok({n_heads, d, ei}, &qk) || !prod_ok({n_heads, dv, ei}, &vy) ||
+        !prod_ok({n_heads, capacity, d, ei}, &kc) || !prod_ok({n_heads, capacity, dv, ei}, &vc) ||
+        la::softmax_decode_splits(pos + 1) > INT32_MAX)
+        return LA_ERR_SHAPE;
+    const int64_t need = la_softmax_decode_workspace_bytes(io_dtype, n_heads, pos + 1, dv);
+    if (need < 0)
+        return LA_ERR_SHAPE;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return LA_ERR_WORKSPACE;
+    if (any_alias({{K_cache, kc}, {V_cache, vc}, {y, vy}, {need > 0 ? workspace : nullptr, need}},
+                  {{q, qk}, {k, qk}, {v, vy}}))
+        return LA_ERR_ALIAS;
+
+    la::SoftmaxDecodeArgs a{q, k, v, n_heads, d, dv, pos, capacity, K_cache, V_cache, scale, y, workspace};
+    (void)hipGetLastError();
+    return launched(la::launch_softmax_decode(a, io_dtype, stream));
 }
 
 }  // extern "C"

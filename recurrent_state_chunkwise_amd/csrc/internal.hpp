@@ -36,6 +36,17 @@ struct DeltaArgs {
     void *y, *S;
 };
 
+struct SoftmaxDecodeArgs {
+    const void *q, *k, *v;
+    int64_t n_heads;
+    int32_t d, dv;
+    int64_t pos, capacity;
+    void *K_cache, *V_cache;
+    double scale;
+    void *y;
+    void *workspace;
+};
+
 // Calls f(std::integral_constant<int, FM>{}) for the feature map `phi` (an
 // la_feature_map the C ABI has already checked), so launchers pick a kernel
 // instantiation per map.
@@ -66,6 +77,9 @@ hipError_t launch_decode(const DecodeArgs &a, la_dtype io_dtype, hipStream_t str
 hipError_t launch_noncausal_general(const PrefillArgs &a, la_dtype io_dtype, hipStream_t stream);
 hipError_t launch_noncausal_mfma_bf16(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_delta_decode(const DeltaArgs &a, la_dtype io_dtype, hipStream_t stream);
+hipError_t launch_softmax_decode(const SoftmaxDecodeArgs &a, la_dtype io_dtype, hipStream_t stream);
+// history pieces (workgroups per head) of the softmax decode for L attended rows
+int64_t softmax_decode_splits(int64_t L);
 
 // True when the bf16 MFMA prefill kernel handles the request.
 bool mfma_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk);

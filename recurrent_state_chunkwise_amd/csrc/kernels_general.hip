@@ -472,18 +472,19 @@ hipError_t launch_noncausal_typed(const PrefillArgs &a, hipStream_t stream)
 // ===================================================================== decode
 constexpr int kDecodeThreads = 512;
 
-// d = dv = 128: one workgroup of 512 threads per state (measured faster than 256 or
-// 1024 on this streaming update).  Thread (rg, cg) owns VEC consecutive columns (cg)
-// of the rows rg, rg + NRG, ..., so each wave reads adjacent full rows; all of a
-// thread's rows are loaded before any is used.
+// d = dv = D (64 or 128): one workgroup of 512 threads per state (measured faster than
+// 256 or 1024 on this streaming update at width 128).  Thread (rg, cg) owns VEC
+// consecutive columns (cg) of the rows rg, rg + NRG, ..., so each wave reads adjacent
+// full rows; all of a thread's rows are loaded before any is used.
 // Each state is touched once per step, so its loads and stores are marked
 // non-temporal to keep it from displacing other lines in the caches.
-template <typename TI, typename TA, int VEC, int FM>
-__global__ __launch_bounds__(kDecodeThreads) void decode_w128_kernel(
+template <typename TI, typename TA, int VEC, int FM, int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_wide_kernel(
     const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v, const TA *__restrict__ alpha,
     TA eps, TI *__restrict__ y, TA *__restrict__ S, TA *__restrict__ z)
 {
-    constexpr int D = 128, DV = 128, NCG = DV / VEC, NRG = kDecodeThreads / NCG, ROWS = D / NRG;
+    constexpr int DV = D, NCG = DV / VEC, NRG = kDecodeThreads / NCG, ROWS = D / NRG;
+    static_assert(ROWS >= 1 && D * NCG * VEC == D * DV, "whole rows per thread group");
     typedef TA vec_t __attribute__((ext_vector_type(VEC)));
     __shared__ TA kf[D], qf[D], vs[DV];
     __shared__ TA red[NRG][DV];
@@ -609,7 +610,12 @@ hipError_t launch_decode_typed(const DecodeArgs &a, hipStream_t stream)
     constexpr int VEC = 16 / sizeof(TA);
     const bool aligned = (reinterpret_cast<uintptr_t>(a.S) % 16) == 0;
     if (a.d == 128 && a.dv == 128 && aligned) {
-        decode_w128_kernel<TI, TA, VEC, FM><<<dim3((unsigned)a.n_states), dim3(kDecodeThreads), 0, stream>>>(
+        decode_wide_kernel<TI, TA, VEC, FM, 128><<<dim3((unsigned)a.n_states), dim3(kDecodeThreads), 0, stream>>>(
+            static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
+            static_cast<const TA *>(a.alpha), static_cast<TA>(a.eps), static_cast<TI *>(a.y),
+            static_cast<TA *>(a.S), static_cast<TA *>(a.z));
+    } else if (a.d == 64 && a.dv == 64 && aligned) {
+        decode_wide_kernel<TI, TA, VEC, FM, 64><<<dim3((unsigned)a.n_states), dim3(kDecodeThreads), 0, stream>>>(
             static_cast<const TI *>(a.q), static_cast<const TI *>(a.k), static_cast<const TI *>(a.v),
             static_cast<const TA *>(a.alpha), static_cast<TA>(a.eps), static_cast<TI *>(a.y),
             static_cast<TA *>(a.S), static_cast<TA *>(a.z));

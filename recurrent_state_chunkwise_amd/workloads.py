@@ -77,6 +77,39 @@ DELTA_DECODE = DecodeConfig(
     "delta_decode_65536_states", requests=128, slots=32, heads=16, d=128, dv=128, seed_writes=0, steps=256,
     eps=0.0, seed=6, note="unit-norm keys, beta = sigmoid(N(0,1)), memories drawn N(0,1)*0.05")
 
+
+
+@dataclass(frozen=True)
+class KvStateConfig:
+    """An explicit K/V history against the fixed recurrent state, one layer: per step every
+    head gets a new (q, k, v); the history path appends it to the K/V caches and attends
+    over all L rows, the state path writes it into S and z and reads them."""
+    name: str
+    batch: int
+    heads: int
+    d: int
+    lengths: tuple
+    warmup: int
+    repeats: int
+    eps: float
+    seed: int
+    note: str = ""
+
+    @property
+    def n_heads(self) -> int:
+        return self.batch * self.heads
+
+
+# the datawhalechina chapter's Step 5 setting: 8 heads x 64, bf16, L in {512, 2048, 8192},
+# warmup 10, repeats 100; and the same at 128 sequences, where the longer histories exceed
+# the last-level cache and the history step is bound by HBM
+KV_STATE = KvStateConfig(
+    "kv_history_vs_fixed_state_h8_d64", batch=1, heads=8, d=64, lengths=(512, 2048, 8192), warmup=10, repeats=100,
+    eps=1e-6, seed=7, note="N(0,1)/sqrt(64) bf16 q, k, v; the history holds L-1 earlier rows, the step adds row L-1")
+KV_STATE_BATCHED = KvStateConfig(
+    "kv_history_vs_fixed_state_b128_h8_d64", batch=128, heads=8, d=64, lengths=(512, 2048, 8192), warmup=10,
+    repeats=100, eps=1e-6, seed=8, note="as above for 128 sequences (1,024 head-states)")
+
 CONFIGS = {c.name: c for c in (SINGLE_HEAD_F64, PREFILL_UNGATED, PREFILL_GATED, DECODE, PREFILL_LONG)}
 
 
@@ -225,3 +258,18 @@ def sampled_states(cfg: DecodeConfig, count: int, seed: int = 12345):
         if int(x) not in must:
             picks.append(int(x))
     return np.array(sorted(set(picks))[:count], dtype=np.int64)
+
+
+def kv_state_history(cfg: KvStateConfig, L: int, device):
+    """The L-1 earlier rows of every head: K, V [n_heads, L-1, d] (bf16), seeded per L."""
+    g = generator(cfg.seed * 100003 + L, device)
+    sc = 1.0 / math.sqrt(cfg.d)
+    return (normal((cfg.n_heads, L - 1, cfg.d), sc, "bf16", g, device),
+            normal((cfg.n_heads, L - 1, cfg.d), sc, "bf16", g, device))
+
+
+def kv_state_steps(cfg: KvStateConfig, L: int, n_steps: int, device):
+    """Per step the new q, k, v of every head ([n_heads, d] bf16), seeded per (L, step)."""
+    g = generator(cfg.seed * 100003 + L + 7919, device)
+    sc = 1.0 / math.sqrt(cfg.d)
+    return [tuple(normal((cfg.n_heads, cfg.d), sc, "bf16", g, device) for _ in range(3)) for _ in range(n_steps)]

@@ -13,7 +13,7 @@ import recurrent_state_chunkwise_amd as la
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "linattn.h")
 
-OK, NULL, SHAPE, DTYPE, EPS, CHUNK, UNSUP, LAUNCH, ALIAS, PHI = range(10)
+OK, NULL, SHAPE, DTYPE, EPS, CHUNK, UNSUP, LAUNCH, ALIAS, PHI, WORKSPACE, SCALE = range(12)
 F64, F32, BF16 = la.LA_F64, la.LA_F32, la.LA_BF16
 
 
@@ -35,13 +35,13 @@ def test_header_symbols_exported(lib):
     names = _declared_functions()
     assert set(names) >= {"la_state_init", "la_prefill_chunked", "la_decode_step", "la_delta_decode_step",
                           "la_status_str", "la_prefill_variant", "la_prefill_chunked_fm", "la_decode_step_fm",
-                          "la_prefill_noncausal"}
+                          "la_prefill_noncausal", "la_softmax_decode_step", "la_softmax_decode_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings(lib):
-    for code in range(10):
+    for code in range(12):
         s = la.la_status_str(code)
         assert isinstance(s, str) and s
     assert la.la_status_str(0) == "ok"
@@ -227,3 +227,39 @@ def test_binding_feature_map_names():
     with pytest.raises(ValueError):
         la.la_prefill_noncausal(q, torch.zeros(1, 1, 2, 3), torch.zeros(1, 1, 2, 1), 1e-6, torch.zeros(1, 1, 2, 1),
                                 torch.zeros(1, 1, 2, 1), torch.zeros(1, 1, 2))
+
+
+def softmax(lib, q=P[0], k=P[1], v=P[2], io=BF16, H=2, d=64, dv=64, pos=10, cap=16, Kc=P[3], Vc=P[4],
+            scale=0.125, y=P[5], ws=P[6], wbytes=1 << 20):
+    return lib.la_softmax_decode_step(q, k, v, io, H, d, dv, pos, cap, Kc, Vc, scale, y, ws, wbytes, None)
+
+
+def test_softmax_decode_workspace_bytes(lib):
+    # one 256-row piece needs no workspace; then n_heads * pieces * (2 + dv) accumulators
+    assert la.la_softmax_decode_workspace_bytes(BF16, 8, 256, 64) == 0
+    assert la.la_softmax_decode_workspace_bytes(BF16, 8, 257, 64) == 8 * 2 * 66 * 4
+    assert la.la_softmax_decode_workspace_bytes(F64, 8, 8192, 64) == 8 * 32 * 66 * 8
+    assert la.la_softmax_decode_workspace_bytes(BF16, 0, 8, 64) == -1
+    assert la.la_softmax_decode_workspace_bytes(BF16, 1, 8, 129) == -1
+
+
+def test_softmax_decode_rejections(lib):
+    assert softmax(lib, q=None) == NULL
+    assert softmax(lib, Kc=None) == NULL
+    assert softmax(lib, y=None) == NULL
+    assert softmax(lib, H=0) == SHAPE
+    assert softmax(lib, pos=-1) == SHAPE
+    assert softmax(lib, pos=16, cap=16) == SHAPE     # pos must lie inside the caches
+    assert softmax(lib, d=0) == SHAPE
+    assert softmax(lib, io=9) == DTYPE
+    assert softmax(lib, d=200) == UNSUP
+    assert softmax(lib, scale=math.nan) == SCALE
+    assert softmax(lib, scale=math.inf) == SCALE
+    # pos = 300: two pieces, so a workspace is required
+    assert softmax(lib, pos=300, cap=512, ws=None) == WORKSPACE
+    assert softmax(lib, pos=300, cap=512, wbytes=100) == WORKSPACE
+    assert softmax(lib, pos=10, ws=None, wbytes=0, y=P[0]) == ALIAS  # no workspace needed at pos 10
+    assert softmax(lib, y=P[0]) == ALIAS
+    assert softmax(lib, Kc=ctypes.c_void_p(P[2].value + 8)) == ALIAS
+    assert softmax(lib, Vc=P[3]) == ALIAS
+    assert softmax(lib, pos=300, cap=512, ws=P[5]) == ALIAS

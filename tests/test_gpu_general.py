@@ -174,7 +174,7 @@ def _decode_case(torch, N, d, dv, gated, io, steps, seed):
 
 
 @pytest.mark.parametrize("io", ["f32", "f64", "bf16"])
-@pytest.mark.parametrize("shape", [(300, 128, 128), (77, 40, 24), (5, 1, 1), (64, 128, 7)])
+@pytest.mark.parametrize("shape", [(300, 128, 128), (130, 64, 64), (77, 40, 24), (5, 1, 1), (64, 128, 7)])
 @pytest.mark.parametrize("gated", [False, True])
 def test_decode_parity(torch, io, shape, gated):
     N, d, dv = shape
