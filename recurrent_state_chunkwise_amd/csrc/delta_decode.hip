@@ -16,7 +16,12 @@ constexpr int kGeneralThreads = 256;
 
 // d = dv = 128: thread (rg, cg) owns VEC consecutive columns (cg) of rows rg, rg + NRG,
 // ..., so each wave reads adjacent full rows; all of a thread's rows are loaded before
-// any is used, with non-temporal hints (each state is touched once per step).
+// any is used, with non-temporal hints (each state is touched once per step).  The
+// read-out of the written state needs no second pass over it: with e the error,
+//   S_new^T q = S^T q + beta (k . q) e,
+// so S^T k and S^T q are reduced together from the state as loaded, and the write
+// follows (one reduction round per step instead of two; the same values up to the
+// order of fp rounding).
 template <typename TI, typename TA, int VEC>
 __global__ __launch_bounds__(kDeltaThreads) void delta_w128_kernel(
     const TI *__restrict__ q, const TI *__restrict__ k, const TI *__restrict__ v, const TA *__restrict__ beta,
@@ -24,8 +29,9 @@ __global__ __launch_bounds__(kDeltaThreads) void delta_w128_kernel(
 {
     constexpr int D = 128, DV = 128, NCG = DV / VEC, NRG = kDeltaThreads / NCG, ROWS = D / NRG;
     typedef TA vec_t __attribute__((ext_vector_type(VEC)));
-    __shared__ TA kf[D], qf[D], vs[DV], be[DV];
-    __shared__ TA red[NRG][DV];
+    __shared__ TA kf[D], qf[D], be[DV];
+    __shared__ TA redk[NRG][DV], redq[NRG][DV];
+    __shared__ TA kq[2];
 
     const int tid = threadIdx.x;
     const int64_t n = blockIdx.x;
@@ -36,64 +42,62 @@ __global__ __launch_bounds__(kDeltaThreads) void delta_w128_kernel(
 #pragma unroll
     for (int i = 0; i < ROWS; ++i)
         s[i] = __builtin_nontemporal_load(&Sv[(rg + i * NRG) * NCG + cg]);
+    TA kqp = TA(0);
     if (tid < D) {
-        kf[tid] = to_acc<TA>(k[n * D + tid]);
-        qf[tid] = to_acc<TA>(q[n * D + tid]);
-        vs[tid] = to_acc<TA>(v[n * DV + tid]);
+        const TA kv = to_acc<TA>(k[n * D + tid]), qv = to_acc<TA>(q[n * D + tid]);
+        kf[tid] = kv;
+        qf[tid] = qv;
+        kqp = kv * qv;
     }
+    const TA vv = tid < DV ? to_acc<TA>(v[n * DV + tid]) : TA(0);
     const TA b = beta[n];
+    kqp = wave_sum(kqp);  // waves 0 and 1 hold k . q over their 64 features
+    if (tid < D && (tid & 63) == 0)
+        kq[tid >> 6] = kqp;
     __syncthreads();
 
-    // prediction p = S^T k: partial sums over this thread's rows
-    TA part[VEC];
+    // S^T k and S^T q: partial sums over this thread's rows of the state as loaded
+    TA pk[VEC], pq[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
-        part[e] = TA(0);
+        pk[e] = pq[e] = TA(0);
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {
-        const TA kv = kf[rg + i * NRG];
+        const TA kv = kf[rg + i * NRG], qv = qf[rg + i * NRG];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            part[e] += kv * s[i][e];
+        for (int e = 0; e < VEC; ++e) {
+            pk[e] += kv * s[i][e];
+            pq[e] += qv * s[i][e];
+        }
     }
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
-        red[rg][cg * VEC + e] = part[e];
+    for (int e = 0; e < VEC; ++e) {
+        redk[rg][cg * VEC + e] = pk[e];
+        redq[rg][cg * VEC + e] = pq[e];
+    }
     __syncthreads();
     if (tid < DV) {
-        TA p = TA(0);
+        TA p = TA(0), o = TA(0);
 #pragma unroll
-        for (int r = 0; r < NRG; ++r)
-            p += red[r][tid];
-        be[tid] = b * (vs[tid] - p);  // beta * error
+        for (int r = 0; r < NRG; ++r) {
+            p += redk[r][tid];
+            o += redq[r][tid];
+        }
+        const TA bev = b * (vv - p);  // beta * error
+        be[tid] = bev;
+        y[n * DV + tid] = from_acc<TI>(o + (kq[0] + kq[1]) * bev);
     }
     __syncthreads();
 
-    // write S += k (beta e)^T, then the read-out y = S^T q from the new state
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-        part[e] = TA(0);
+    // write S += k (beta e)^T
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {
         const int f = rg + i * NRG;
-        const TA kv = kf[f], qv = qf[f];
+        const TA kv = kf[f];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
+        for (int e = 0; e < VEC; ++e)
             s[i][e] += kv * be[cg * VEC + e];
-            part[e] += qv * s[i][e];
-        }
         __builtin_nontemporal_store(s[i], &Sv[f * NCG + cg]);
-    }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-        red[rg][cg * VEC + e] = part[e];
-    __syncthreads();
-    if (tid < DV) {
-        TA acc = TA(0);
-#pragma unroll
-        for (int r = 0; r < NRG; ++r)
-            acc += red[r][tid];
-        y[n * DV + tid] = from_acc<TI>(acc);
     }
 }
 
