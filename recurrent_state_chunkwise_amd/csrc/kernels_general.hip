@@ -15,40 +15,64 @@ namespace {
 constexpr int kThreads = 256;
 
 // ===================================================================== state init
-// Zero fill in three parts so the bulk uses aligned 16-byte stores.
-__global__ __launch_bounds__(kThreads) void zero_fill_kernel(unsigned char *__restrict__ head, int64_t n_head,
-                                                             uint4 *__restrict__ bulk, int64_t n_bulk,
-                                                             unsigned char *__restrict__ tail, int64_t n_tail)
+// One launch zeroes up to two byte ranges (S and z).  Each range is cut into an
+// unaligned head, a bulk of aligned 16-byte stores and a tail; the first blocks of the
+// grid take the first range and the rest the second.
+struct FillRange {
+    unsigned char *head;
+    int64_t n_head;
+    uint4 *bulk;
+    int64_t n_bulk;
+    unsigned char *tail;
+    int64_t n_tail;
+    int64_t blocks;  // blocks of the grid given to this range
+};
+
+FillRange make_fill_range(void *p, int64_t nbytes)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    for (int64_t i = i0; i < n_bulk; i += stride)
-        bulk[i] = zero;
-    for (int64_t i = i0; i < n_head; i += stride)
-        head[i] = 0;
-    for (int64_t i = i0; i < n_tail; i += stride)
-        tail[i] = 0;
+    FillRange r;
+    unsigned char *b = static_cast<unsigned char *>(p);
+    r.n_head = (int64_t)((16 - (reinterpret_cast<uintptr_t>(b) & 15)) & 15);
+    if (r.n_head > nbytes)
+        r.n_head = nbytes;
+    r.n_bulk = (nbytes - r.n_head) / 16;
+    r.n_tail = nbytes - r.n_head - r.n_bulk * 16;
+    r.head = b;
+    r.bulk = reinterpret_cast<uint4 *>(b + r.n_head);
+    r.tail = b + r.n_head + r.n_bulk * 16;
+    int64_t work = r.n_bulk > r.n_head ? r.n_bulk : r.n_head;
+    if (r.n_tail > work)
+        work = r.n_tail;
+    r.blocks = (work + kThreads - 1) / kThreads;
+    if (r.blocks > 8192)
+        r.blocks = 8192;
+    return r;
 }
 
-hipError_t zero_fill(void *p, int64_t nbytes, hipStream_t stream)
+__global__ __launch_bounds__(kThreads) void zero_fill_kernel(FillRange r0, FillRange r1)
 {
-    unsigned char *b = static_cast<unsigned char *>(p);
-    int64_t n_head = (int64_t)((16 - (reinterpret_cast<uintptr_t>(b) & 15)) & 15);
-    if (n_head > nbytes)
-        n_head = nbytes;
-    const int64_t n_bulk = (nbytes - n_head) / 16;
-    const int64_t n_tail = nbytes - n_head - n_bulk * 16;
-    int64_t work = n_bulk > n_head ? n_bulk : n_head;
-    if (n_tail > work)
-        work = n_tail;
-    int64_t blocks = (work + kThreads - 1) / kThreads;
-    if (blocks > 16384)
-        blocks = 16384;
-    if (blocks < 1)
-        blocks = 1;
-    zero_fill_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(
-        b, n_head, reinterpret_cast<uint4 *>(b + n_head), n_bulk, b + n_head + n_bulk * 16, n_tail);
+    const bool first = (int64_t)blockIdx.x < r0.blocks;
+    const FillRange &r = first ? r0 : r1;
+    const int64_t blk = first ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - r0.blocks;
+    const int64_t stride = r.blocks * kThreads;
+    const int64_t i0 = blk * kThreads + threadIdx.x;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t i = i0; i < r.n_bulk; i += stride)
+        r.bulk[i] = zero;
+    for (int64_t i = i0; i < r.n_head; i += stride)
+        r.head[i] = 0;
+    for (int64_t i = i0; i < r.n_tail; i += stride)
+        r.tail[i] = 0;
+}
+
+hipError_t zero_fill2(void *p0, int64_t n0, void *p1, int64_t n1, hipStream_t stream)
+{
+    const FillRange r0 = make_fill_range(p0, n0);
+    const FillRange r1 = make_fill_range(p1, n1);
+    const int64_t blocks = r0.blocks + r1.blocks;
+    if (blocks == 0)
+        return hipSuccess;
+    zero_fill_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, stream>>>(r0, r1);
     return hipGetLastError();
 }
 
@@ -634,10 +658,7 @@ hipError_t launch_state_init(void *S, void *z, int64_t n_states, int32_t r, int3
                              hipStream_t stream)
 {
     const int64_t es = state_dtype == LA_F64 ? 8 : 4;
-    hipError_t e = zero_fill(S, n_states * r * dv * es, stream);
-    if (e != hipSuccess)
-        return e;
-    return zero_fill(z, n_states * r * es, stream);
+    return zero_fill2(S, n_states * r * dv * es, z, n_states * r * es, stream);
 }
 
 hipError_t launch_prefill_general(const PrefillArgs &a, la_dtype io_dtype, hipStream_t stream)

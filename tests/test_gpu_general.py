@@ -54,6 +54,15 @@ def test_state_init(torch):
     torch.cuda.synchronize()
     h = buf.cpu()
     assert h[0] == 7.0 and h[-1] == 7.0 and (h[1:-1] == 0).all()
+    # both ranges span many blocks, each with an unaligned head and a tail
+    n, r, dv = 1000, 33, 17
+    buf = torch.full((1 + n * r * dv + n * r + 1,), 7.0, device="cuda", dtype=torch.float32)
+    S = buf[1:1 + n * r * dv].view(n, r, dv)
+    z = buf[1 + n * r * dv:1 + n * r * dv + n * r].view(n, r)
+    la.la_state_init(S, z)
+    torch.cuda.synchronize()
+    h = buf.cpu()
+    assert h[0] == 7.0 and h[-1] == 7.0 and (h[1:-1] == 0).all()
 
 
 @pytest.mark.parametrize("chunk", [1, 7, 16, 64])
