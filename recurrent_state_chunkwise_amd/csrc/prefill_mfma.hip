@@ -589,6 +589,11 @@ constexpr int kPcThreads = kPcConsumers + 64 * kPcProducers;
 constexpr int kSumProducers = LA_SUM_PRODUCERS;  // producer waves of the segment-map pass
 static_assert(kSumProducers == 4 || kSumProducers == 8, "4 or 8 producer waves");
 constexpr int kSumThreads = kPcConsumers + 64 * kSumProducers;
+#ifndef LA_SUM_SETS
+#define LA_SUM_SETS 2
+#endif
+constexpr int kSumSets = LA_SUM_SETS;  // chunks of K and V in flight per producer thread
+static_assert(kSumSets == 2 || kSumSets == 4, "2 or 4 register sets");
 
 constexpr int kRow = kD + 8;  // padded token row, in elements
 __device__ __forceinline__ int pr_off(int row, int col) { return row * kRow + col; }
@@ -1072,7 +1077,8 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
     const int64_t s0 = (int64_t)seg * a.seg_len;
     const int64_t len = seg == a.nseg - 1 ? a.T - s0 : a.seg_len;
     const int n_chunks = (int)((len + C - 1) / C);
-    const int n_steps = (n_chunks + 1) & ~1;  // both roles walk an even number of chunk steps
+    // both roles walk the same number of chunk steps, a multiple of the register sets
+    const int n_steps = (n_chunks + kSumSets - 1) / kSumSets * kSumSets;
     auto chunk_len = [&](int c) { return (int)min((int64_t)C, len - (int64_t)c * C); };
     const int64_t row0 = head * a.T + s0;
 
@@ -1086,23 +1092,23 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
         constexpr int TPT = 16 / kSumProducers;  // tokens per thread and chunk
         const int fg = pt & 15, tg = pt >> 4;    // granule fg of tokens TPT tg .. TPT tg + TPT - 1
         const int ld_off = tg * TPT * kD * 2 + fg * 16;
-        uint4 rk0[TPT], rv0[TPT], rk1[TPT], rv1[TPT];
-        float ar0 = 0.f, ar1 = 0.f;  // alpha of even / odd chunks
+        uint4 rk[kSumSets][TPT], rv[kSumSets][TPT];  // chunk c in set c % kSumSets
+        float ar[2] = {0.f, 0.f};                      // alpha of even / odd chunks
 
-        auto load_kv = [&](int c, uint4 (&rk)[TPT], uint4 (&rv)[TPT]) {
+        auto load_kv = [&](int c, uint4 (&rkx)[TPT], uint4 (&rvx)[TPT]) {
 #pragma unroll
             for (int p = 0; p < TPT; ++p) {
-                rk[p] = bload16(rK, c * C * kD * 2 + ld_off + p * kD * 2);
-                rv[p] = bload16(rV, c * C * kD * 2 + ld_off + p * kD * 2);
+                rkx[p] = bload16(rK, c * C * kD * 2 + ld_off + p * kD * 2);
+                rvx[p] = bload16(rV, c * C * kD * 2 + ld_off + p * kD * 2);
             }
         };
-        auto load_a = [&](int c, float &ar) {  // every producer wave loads; the scanner uses it
+        auto load_a = [&](int c, float &arx) {  // every producer wave loads; the scanner uses it
             if (GATED)
-                ar = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (c * C + lane) * 4, 0, 0));
+                arx = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (c * C + lane) * 4, 0, 0));
         };
-        auto scan = [&](int n, int gs, float ar) {
+        auto scan = [&](int n, int gs, float arx) {
             if (GATED && scanner) {
-                const float av = lane < n ? ar : 1.f;
+                const float av = lane < n ? arx : 1.f;
                 float s = av > 0.f ? __logf(av) : 0.f;
                 int zf = av == 0.f ? lane : -1;
 #pragma unroll
@@ -1119,7 +1125,7 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                 sm.gj[gs][lane] = zf >= 0 ? 0.f : __expf(s);
             }
         };
-        auto stage = [&](int buf, int gs, int n, const uint4 (&rk)[TPT], const uint4 (&rv)[TPT]) {
+        auto stage = [&](int buf, int gs, int n, const uint4 (&rkx)[TPT], const uint4 (&rvx)[TPT]) {
 #pragma unroll
             for (int p = 0; p < TPT; ++p) {
                 const int j = tg * TPT + p;
@@ -1127,7 +1133,7 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                                        : (GATED ? (sm.zp[gs][n - 1] > j ? 0.f : __expf(sm.lg[gs][n - 1] - sm.lg[gs][j]))
                                                 : 1.f);
                 float x[8];
-                unpack8(rk[p], x);
+                unpack8(rkx[p], x);
                 bf16x8 kb;
 #pragma unroll
                 for (int s = 0; s < 8; ++s)
@@ -1136,40 +1142,44 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                 if (!GATED && j >= n)
                     u = make_uint4(0u, 0u, 0u, 0u);
                 *reinterpret_cast<uint4 *>(&sm.Ws[buf][pr_off(j, fg * 8)]) = u;
-                *reinterpret_cast<uint4 *>(&sm.Vs[buf][pr_off(j, fg * 8)]) = rv[p];
+                *reinterpret_cast<uint4 *>(&sm.Vs[buf][pr_off(j, fg * 8)]) = rvx[p];
             }
         };
-        // interval i: stage chunk i + 1 from its set and refill the set with chunk i + 3;
-        // scan the gates of chunk i + 2 and load the alpha of chunk i + 4 in its place.
-        // Loads past the end of the segment read zeros through the buffer resource; they
-        // are issued unconditionally so that every wait on them is a counted one.
-        auto step = [&](int i, uint4 (&rk)[TPT], uint4 (&rv)[TPT], float &ar) {
+        // interval i: stage chunk i + 1 from its set and refill the set with chunk
+        // i + 1 + kSumSets; scan the gates of chunk i + 2 and load the alpha of chunk i + 4
+        // in its place.  Loads past the end of the segment read zeros through the buffer
+        // resource; they are issued unconditionally so that every wait on them is a
+        // counted one.
+        auto step = [&](int i, uint4 (&rkx)[TPT], uint4 (&rvx)[TPT], float &arx) {
             const int cn = i + 1;
             if (cn < n_chunks)
-                stage(cn & 1, cn % 3, chunk_len(cn), rk, rv);
-            load_kv(cn + 2, rk, rv);
+                stage(cn & 1, cn % 3, chunk_len(cn), rkx, rvx);
+            load_kv(cn + kSumSets, rkx, rvx);
             if (i + 2 < n_chunks)
-                scan(chunk_len(i + 2), (i + 2) % 3, ar);
-            load_a(i + 4, ar);
+                scan(chunk_len(i + 2), (i + 2) % 3, arx);
+            load_a(i + 4, arx);
             wg_barrier();  // chunk i done, chunk i + 1 staged
         };
 
-        load_kv(0, rk0, rv0);
-        load_a(0, ar0);
-        load_kv(1, rk1, rv1);
-        load_a(1, ar1);
-        scan(chunk_len(0), 0, ar0);
+#pragma unroll
+        for (int c = 0; c < kSumSets; ++c) {
+            load_kv(c, rk[c], rv[c]);
+            if (c < 2)
+                load_a(c, ar[c]);
+        }
+        scan(chunk_len(0), 0, ar[0]);
         if (n_chunks > 1)
-            scan(chunk_len(1), 1, ar1);
-        load_a(2, ar0);
-        load_a(3, ar1);
+            scan(chunk_len(1), 1, ar[1]);
+        load_a(2, ar[0]);
+        load_a(3, ar[1]);
         wg_barrier();
-        stage(0, 0, chunk_len(0), rk0, rv0);
-        load_kv(2, rk0, rv0);
+        stage(0, 0, chunk_len(0), rk[0], rv[0]);
+        load_kv(kSumSets, rk[0], rv[0]);
         wg_barrier();
-        for (int i = 0; i < n_steps; i += 2) {
-            step(i, rk1, rv1, ar0);  // stages chunk i + 1 (odd), scans chunk i + 2 (even)
-            step(i + 1, rk0, rv0, ar1);
+        for (int i = 0; i < n_steps; i += kSumSets) {
+#pragma unroll
+            for (int u = 0; u < kSumSets; ++u)  // stages chunk i + u + 1, scans chunk i + u + 2
+                step(i + u, rk[(u + 1) % kSumSets], rv[(u + 1) % kSumSets], ar[u & 1]);
         }
         return;
     }
@@ -1191,9 +1201,9 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
     wg_barrier();
     wg_barrier();
     for (int i = 0; i < n_steps; ++i) {
-        if (i >= n_chunks) {  // the trailing empty step of an odd chunk count
+        if (i >= n_chunks) {  // trailing empty steps up to a multiple of the register sets
             wg_barrier();
-            break;
+            continue;
         }
         const int buf = i & 1;
         const bf16 *Wb = sm.Ws[buf];

@@ -89,6 +89,9 @@ CASES = [
     (1, 4, 1600, 128, False, False),
     (2, 8, 700, 64, True, False),
     (1, 16, 1300, 128, True, True),
+    # more segments than the scan reads in one batch
+    (1, 1, 4000, 64, True, True),
+    (1, 1, 5000, 128, False, True),
 ]
 
 
@@ -136,6 +139,25 @@ def test_mfma_deterministic(torch):
     r2 = _run(torch, Q, K, V, alpha, 128, S0, z0)
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("chunk,gated", [(64, False), (64, True), (128, True)])
+def test_mfma_unaligned_state_bitwise(torch, chunk, gated):
+    """S and z that are 4- but not 16-byte aligned give the aligned results bit for bit
+    (several segments, so the entering states go through the segment scan)."""
+    Q, K, V, alpha, S0, z0 = _inputs(torch, 1, 2, 2048, gated, True, 12)
+    Y, S, z = _run(torch, Q, K, V, alpha, chunk, S0, z0)
+    nS, nz = S0.numel(), z0.numel()
+    buf = torch.empty(1 + nS + 1 + nz, device="cuda")
+    Su = buf[1:1 + nS].view(S0.shape)
+    zu = buf[2 + nS:2 + nS + nz].view(z0.shape)
+    assert Su.data_ptr() % 16 != 0 and zu.data_ptr() % 16 != 0
+    Su.copy_(S0)
+    zu.copy_(z0)
+    Yu = torch.empty_like(V)
+    la.la_prefill_chunked(Q, K, V, alpha, 1e-6, chunk, Yu, Su, zu)
+    torch.cuda.synchronize()
+    assert torch.equal(Yu, Y) and torch.equal(Su, S) and torch.equal(zu, z)
 
 
 def test_mfma_resume_matches_single_call(torch):

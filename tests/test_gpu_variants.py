@@ -166,6 +166,7 @@ NONCAUSAL = [
     (1, 2, 700, 128, 128, "bf16", True),       # two segments, ragged last one
     (1, 1, 2000, 128, 128, "bf16", False),     # six segments, two read-out blocks
     (1, 1, 1041, 128, 128, "bf16", True),      # read-out block boundary + ragged tile
+    (1, 1, 4100, 128, 128, "bf16", True),      # twelve segments: the sum reads its slots in two batches
     (2, 2, 90, 16, 24, "f32", True),
     (1, 2, 40, 8, 12, "f64", True),
     (1, 2, 100, 64, 128, "bf16", False),       # bf16 at another width: general kernel
