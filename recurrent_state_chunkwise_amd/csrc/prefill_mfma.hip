@@ -1070,8 +1070,12 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
     const int lr = lane & 15;
     const int lg4 = lane >> 4;
 
-    const int64_t head = blockIdx.x / a.nseg;
-    const int seg = blockIdx.x % a.nseg;
+    // Segment-major block order: workgroup b runs on XCD b mod 8, so numbering
+    // (sequence, segment) head-major would put every idle last-segment workgroup on the
+    // same XCDs whenever the segment count divides 8; segment-major spreads them evenly.
+    const int64_t n_heads = gridDim.x / a.nseg;
+    const int64_t head = blockIdx.x % n_heads;
+    const int seg = (int)(blockIdx.x / n_heads);
     if (!NONCAUSAL && seg == a.nseg - 1)
         return;  // the last segment's map is never needed
     const int64_t s0 = (int64_t)seg * a.seg_len;
