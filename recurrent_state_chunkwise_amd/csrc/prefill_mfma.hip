@@ -103,9 +103,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
+// Cache policy operand of the buffer accesses: kNT marks an access non-temporal (the `nt`
+// bit), for data read for the last time or written and not read back by the library:
+// such lines are not kept in the caches, where the output rows would otherwise wait,
+// dirty, to be written back during the next kernel.
+constexpr int kNT = 2;
+template <int POL = 0>
 __device__ __forceinline__ uint4 bload16(rsrc_t r, int off)
 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -243,14 +249,14 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
         const int off = chunk * C * kD * 2 + ld_off;
 #pragma unroll
         for (int p = 0; p < G::TPT; ++p)
-            raw_k[p] = bload16(rK, off + p * kD * 2);
+            raw_k[p] = bload16<kNT>(rK, off + p * kD * 2);
     };
     auto prefetch_qv = [&](int chunk) {
         const int off = chunk * C * kD * 2 + ld_off;
 #pragma unroll
         for (int p = 0; p < G::TPT; ++p) {
-            raw_q[p] = bload16(rQ, off + p * kD * 2);
-            raw_v[p] = bload16(rV, off + p * kD * 2);
+            raw_q[p] = bload16<kNT>(rQ, off + p * kD * 2);
+            raw_v[p] = bload16<kNT>(rV, off + p * kD * 2);
         }
     };
     auto prefetch_a = [&](int chunk) {
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 #pragma unroll
             for (int h = 0; h < C / 64; ++h)
                 araw[h] = __uint_as_float(
-                    (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (chunk * C + h * 64 + lane) * 4, 0, 0));
+                    (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (chunk * C + h * 64 + lane) * 4, 0, kNT));
         }
     };
 
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
             // rows past the end of the segment fall outside rY and are dropped
             const int off = (int)((t0 + j) * kD + fw) * 2;
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, yb),
-                                                  rY, off, 0, 0);
+                                                  rY, off, 0, kNT);
         }
     };
     // (4) S = g_end S + (w K~)^T V for this wave's columns, and
@@ -700,18 +706,18 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         auto load_qv = [&](int c, uint4 (&rq)[TPT], uint4 (&rv)[TPT]) {
 #pragma unroll
             for (int p = 0; p < TPT; ++p) {
-                rq[p] = bload16(rQ, c * C * kD * 2 + ld_off + p * kD * 2);
-                rv[p] = bload16(rV, c * C * kD * 2 + ld_off + p * kD * 2);
+                rq[p] = bload16<kNT>(rQ, c * C * kD * 2 + ld_off + p * kD * 2);
+                rv[p] = bload16<kNT>(rV, c * C * kD * 2 + ld_off + p * kD * 2);
             }
         };
         auto load_k = [&](int c, uint4 (&rk)[TPT]) {
 #pragma unroll
             for (int p = 0; p < TPT; ++p)
-                rk[p] = bload16(rK, c * C * kD * 2 + ld_off + p * kD * 2);
+                rk[p] = bload16<kNT>(rK, c * C * kD * 2 + ld_off + p * kD * 2);
         };
         auto load_a = [&](int c, float &ar) {  // every producer wave loads; the scanner uses it
             if (GATED)
-                ar = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (c * C + lane) * 4, 0, 0));
+                ar = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (c * C + lane) * 4, 0, kNT));
         };
         // inclusive scans of log(alpha) and of the last zero-gate position (one wave)
         auto scan = [&](int n, int gs, float ar) {
@@ -787,7 +793,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 const uint4 v = *reinterpret_cast<const uint4 *>(&ys[row * kD + g * 8]);
                 const int off = ((c * C + row) * kD + ((g ^ (row & 15)) << 3)) * 2;
                 __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), rY, off, 0, 0);
+                    __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), rY, off, 0, kNT);
             }
         };
         // one chunk interval: write out y of chunk i - 1, stage chunk cn = i + 1 from its
@@ -1102,8 +1108,8 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
         auto load_kv = [&](int c, uint4 (&rkx)[TPT], uint4 (&rvx)[TPT]) {
 #pragma unroll
             for (int p = 0; p < TPT; ++p) {
-                rkx[p] = bload16(rK, c * C * kD * 2 + ld_off + p * kD * 2);
-                rvx[p] = bload16(rV, c * C * kD * 2 + ld_off + p * kD * 2);
+                rkx[p] = bload16<NONCAUSAL ? kNT : 0>(rK, c * C * kD * 2 + ld_off + p * kD * 2);
+                rvx[p] = bload16<NONCAUSAL ? kNT : 0>(rV, c * C * kD * 2 + ld_off + p * kD * 2);
             }
         };
         auto load_a = [&](int c, float &arx) {  // every producer wave loads; the scanner uses it
