@@ -326,8 +326,8 @@ def cpu_baseline(wl, torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the decode and gated workloads")
     ap.add_argument("--only", choices=["prefill", "noncausal", "decode", "delta", "kvstate", "copy"], default=None,
@@ -462,8 +462,9 @@ def main():
         out["kv_vs_state_batched"] = time_kv_state(torch, la, wl, wl.KV_STATE_BATCHED)
         other = []
         for ocfg in (wl.PREFILL_GATED, wl.PREFILL_LONG):
-            steps = 10 if ocfg.T <= 16384 else 3
-            o_total, o_call, _ = time_prefill(torch, la, wl, ocfg, steps, 2)
+            # about 30 ms of warm-up: the clock settles only after some tens of ms of load
+            steps, warm = (150, 150) if ocfg.T <= 16384 else (16, 16)
+            o_total, o_call, _ = time_prefill(torch, la, wl, ocfg, steps, warm)
             ob = prefill_bytes(ocfg.B, ocfg.H, ocfg.T, ocfg.gated)
             of = prefill_useful_flops(ocfg.B, ocfg.H, ocfg.T, ocfg.chunk)
             other.append({"workload": ocfg.name, "value": ocfg.B * ocfg.T / (o_call / 1e3), "unit": "tokens/s",
