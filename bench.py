@@ -21,7 +21,7 @@ line also carries:
   cpu_baseline  the FP64 oracle timed on this host's cores on a sample of the
                 prefill workload.
 Run: python bench.py [--gpus 1] [--steps K] [--warmup W]
-     python bench.py --only prefill|noncausal|decode|delta|kvstate|copy   (one workload, for profiler runs; `copy`
+     python bench.py --only prefill|noncausal|gated|long|decode|delta|kvstate|copy   (one workload, for profiler runs; `copy`
      is a plain 1 GiB device-to-device copy used to calibrate the HBM byte counters)
 """
 from __future__ import annotations
@@ -330,7 +330,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the decode and gated workloads")
-    ap.add_argument("--only", choices=["prefill", "noncausal", "decode", "delta", "kvstate", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "noncausal", "gated", "long", "decode", "delta", "kvstate", "copy"],
+                    default=None,
                     help="run one workload only and print its timing (for profiler runs)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="steps to time with --only decode or --only delta (default: the workload's)")
@@ -369,6 +370,12 @@ def main():
     if args.only == "kvstate":
         print(json.dumps({"only": "kvstate", "kv_vs_state": time_kv_state(torch, la, wl, wl.KV_STATE),
                           "kv_vs_state_batched": time_kv_state(torch, la, wl, wl.KV_STATE_BATCHED)}))
+        return
+    if args.only in ("gated", "long"):
+        ocfg = wl.PREFILL_GATED if args.only == "gated" else wl.PREFILL_LONG
+        o_total, o_call, _ = time_prefill(torch, la, wl, ocfg, args.steps, args.warmup)
+        print(json.dumps({"only": args.only, "workload": ocfg.name, "steps": args.steps,
+                          "ms_per_step": o_total / args.steps, "call_ms": o_call}))
         return
     cfg = wl.PREFILL_UNGATED
     if args.only == "noncausal":

@@ -119,6 +119,47 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, int off)
 __device__ __forceinline__ unsigned pack_lo(unsigned x, unsigned y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
 __device__ __forceinline__ unsigned pack_hi(unsigned x, unsigned y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
 
+// Gate weights inside a chunk, from lg (the in-chunk prefix sums of log alpha, zero gates
+// left out) and zp (the position of the last zero gate at or before each token, -1 if
+// none).  The weight of token i's write as token j reads it (i <= j) is the product of
+// the gates of tokens i+1..j: 0 if one of them is zero, else exp(lg_j - lg_i).  Both
+// helpers read everything they need and evaluate the exponentials unconditionally, then
+// select, so that their LDS reads are issued together rather than one behind another in
+// branches; for i > j the exponential may overflow and is discarded by the caller.
+template <bool GATED>
+__device__ __forceinline__ void pair_decays(const float *lg, const int *zp, int j, const int (&i)[4], float (&dec)[4])
+{
+    if (!GATED) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dec[r] = 1.f;
+        return;
+    }
+    const float lgj = lg[j];
+    const int zpj = zp[j];
+    float lgi[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        lgi[r] = lg[i[r]];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float e = __expf(lgj - lgi[r]);
+        dec[r] = zpj > i[r] ? 0.f : e;
+    }
+}
+// write weight of token j of a chunk of n tokens: the gates after j to the chunk end;
+// 0 past the end of the chunk (where the tokens read as zeros)
+template <bool GATED>
+__device__ __forceinline__ float write_weight(const float *lg, const int *zp, int n, int j)
+{
+    float w = 1.f;
+    if (GATED) {
+        const float e = __expf(lg[n - 1] - lg[j]);
+        w = zp[n - 1] > j ? 0.f : e;
+    }
+    return j >= n ? 0.f : w;
+}
+
 template <int C>
 struct Cfg {
     static constexpr int NTJ = C / 16;                 // 16-token tiles per chunk
@@ -299,10 +340,6 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
             }
         }
     };
-    auto pair_decay = [&](int gs, int j, int i) -> float {  // gates of tokens i+1..j
-        return sm.zp[gs][j] > i ? 0.f : __expf(sm.lg[gs][j] - sm.lg[gs][i]);
-    };
-
     // ---------------------------------------------------------------- staging
     // keys: phi, row-major K~ for the scores and the token-major write weights
     // w_j phi(k_j) (w_j = gates after j to the chunk end, 0 past the end of the segment,
@@ -312,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
 #pragma unroll
         for (int p = 0; p < G::TPT; ++p) {
             const int j = tg * G::TPT + p;
-            const float w = j >= n ? 0.f : (GATED ? pair_decay(gs, n - 1, j) : 1.f);
+            const float w = write_weight<GATED>(sm.lg[gs], sm.zp[gs], n, j);
             float x[8];
             unpack8(raw_k[p], x);
             bf16x8 kb;
@@ -391,6 +428,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
             while ((tj + 1) * (tj + 2) / 2 <= k)
                 ++tj;
             const int ti = k - tj * (tj + 1) / 2;
+            const int j = tj * 16 + lr;
+            int ii[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ii[r] = ti * 16 + lg4 * 4 + r;
+            float dec[4];
+            pair_decays<GATED>(sm.lg[gs], sm.zp[gs], j, ii, dec);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kf = 0; kf < 4; ++kf) {
@@ -398,16 +442,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                 const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&sm.Qs[qk_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
                 acc = mfma(ka, qb, acc);
             }
-            const int j = tj * 16 + lr;
             bf16x4 pk;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ti * 16 + lg4 * 4 + r;
-                float v = i <= j ? acc[r] : 0.f;
-                if (GATED && i <= j)
-                    v *= pair_decay(gs, j, i);
-                pk[r] = static_cast<bf16>(v);
-            }
+            for (int r = 0; r < 4; ++r)
+                pk[r] = static_cast<bf16>(ii[r] <= j ? acc[r] * dec[r] : 0.f);
             sm.P[k * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
         }
     };
@@ -682,10 +720,6 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
     auto chunk_len = [&](int c) { return (int)min((int64_t)C, len - (int64_t)c * C); };
     const int64_t row0 = head * a.T + s0;
 
-    auto pair_decay = [&](int gs, int j, int i) -> float {  // gates of tokens i+1..j
-        return sm.zp[gs][j] > i ? 0.f : __expf(sm.lg[gs][j] - sm.lg[gs][i]);
-    };
-
     if (wave >= 8) {
         // ============================================================ producers
         const rsrc_t rQ = make_rsrc(a.Q + row0 * kD, len * kD * 2);
@@ -765,7 +799,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 float x[8];
                 unpack8(rk[p], x);
                 bf16x8 kb, kwb;
-                const float w = j >= n ? 0.f : (GATED ? pair_decay(gs, n - 1, j) : 1.f);
+                const float w = write_weight<GATED>(sm.lg[gs], sm.zp[gs], n, j);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     const float f = phi<FM>(x[s]);
@@ -900,6 +934,14 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
             while ((tj + 1) * (tj + 2) / 2 <= k)
                 ++tj;
             const int ti = k - tj * (tj + 1) / 2;
+            // acc[r] = score (j = 16tj + lr, i = 16ti + sigma(4lg4 + r))
+            const int j = tj * 16 + lr;
+            int ii[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ii[r] = ti * 16 + sigma(lg4 * 4 + r);
+            float dec[4];
+            pair_decays<GATED>(sm.lg[buf], sm.zp[buf], j, ii, dec);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kf = 0; kf < 4; ++kf) {
@@ -907,17 +949,10 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&Qb[pr_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
                 acc = mfma(ka, qb, acc);
             }
-            // acc[r] = score (j = 16tj + lr, i = 16ti + sigma(4lg4 + r))
-            const int j = tj * 16 + lr;
             bf16x4 pk;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ii = ti * 16 + sigma(lg4 * 4 + r);
-                float v = ii <= j ? acc[r] : 0.f;
-                if (GATED && ii <= j)
-                    v *= pair_decay(buf, j, ii);
-                pk[r] = static_cast<bf16>(v);
-            }
+            for (int r = 0; r < 4; ++r)
+                pk[r] = static_cast<bf16>(ii[r] <= j ? acc[r] * dec[r] : 0.f);
             reinterpret_cast<uint2 *>(&sm.P[(kPairBase[tj] + (ti >> 1)) * 64 + lane])[ti & 1] =
                 *reinterpret_cast<uint2 *>(&pk);
         }
@@ -1139,9 +1174,7 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
 #pragma unroll
             for (int p = 0; p < TPT; ++p) {
                 const int j = tg * TPT + p;
-                const float w = j >= n ? 0.f
-                                       : (GATED ? (sm.zp[gs][n - 1] > j ? 0.f : __expf(sm.lg[gs][n - 1] - sm.lg[gs][j]))
-                                                : 1.f);
+                const float w = write_weight<GATED>(sm.lg[gs], sm.zp[gs], n, j);
                 float x[8];
                 unpack8(rkx[p], x);
                 bf16x8 kb;
