@@ -145,6 +145,7 @@ __device__ __forceinline__ void pair_decays(const float *lg, const int *zp, int 
     for (int r = 0; r < 4; ++r) {
         const float e = __expf(lgj - lgi[r]);
         dec[r] = zpj > i[r] ? 0.f : e;
+        asm volatile("" : "+v"(dec[r]));  // computed here, not sunk into the caller's i <= j branch
     }
 }
 // write weight of token j of a chunk of n tokens: the gates after j to the chunk end;
