@@ -473,7 +473,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                 zb[kf][4 + r] = static_cast<bf16>(zhi[r]);
             }
         }
-#pragma unroll 1
+        // two token tiles per iteration: their chains overlap (unrolling further spills)
+#pragma unroll 2
         for (int tj = 0; tj < G::NTJ; ++tj) {
             const int j = tj * 16 + lr;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f}, dac = {0.f, 0.f, 0.f, 0.f};
