@@ -111,6 +111,20 @@ def test_mfma_zero_gates_reset(torch, chunk):
     _check(Y, S, z, oracle_prefill(Q, K, V, alpha, 1e-6, S0, z0), "zero gates chunk=%d" % chunk)
 
 
+@pytest.mark.parametrize("chunk,T", [(64, 300), (128, 300), (64, 2000), (128, 2100)])
+def test_mfma_tiny_gates(torch, chunk, T):
+    """Gates spread from about 1 down to the fp32 subnormal range (sigmoid of N(0, 30), a few
+    exactly 0): the in-chunk log sums reach thousands below zero, the exponentials above
+    the diagonal overflow and must be discarded, and products of gates underflow."""
+    Q, K, V, alpha, S0, z0 = _inputs(torch, 1, 2, T, True, True, 31 + T + chunk)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 + T + chunk)
+    alpha = torch.sigmoid(torch.randn(alpha.shape, generator=g, device="cuda") * 30.0)
+    assert float(alpha.min()) < 1e-30 and float(alpha.max()) > 0.999
+    Y, S, z = _run(torch, Q, K, V, alpha, chunk, S0, z0)
+    _check(Y, S, z, oracle_prefill(Q, K, V, alpha, 1e-6, S0, z0), "tiny gates chunk=%d T=%d" % (chunk, T))
+
+
 def test_mfma_causality_bitwise(torch):
     Q, K, V, alpha, S0, z0 = _inputs(torch, 1, 2, 256, True, True, 5)
     Y1, _, _ = _run(torch, Q, K, V, alpha, 64, S0, z0)
