@@ -18,6 +18,9 @@ line also carries:
                 recurrent state (one decode step), 8 heads x 64, bf16, L = 512, 2048,
                 8192: state bytes, step time, peak memory; also at 128 sequences;
   other         the gated prefill workloads, timed the same way;
+  measured_ceilings  what torch's own copy, reduction, fill and bf16 matmul reach on this GPU; the
+                prefill and decode rooflines also carry their fraction of the measured stream rate
+                for their read/write mix (`frac_of_measured`);
   cpu_baseline  the FP64 oracle timed on this host's cores on a sample of the
                 prefill workload.
 Run: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -294,6 +297,60 @@ def time_kv_state(torch, la, wl, cfg):
             "rows": rows}
 
 
+def measured_ceilings(torch, reps=10):
+    """What this GPU reaches on plain streams and a dense product, with torch's own kernels:
+    a 1:1 device copy, a read-only reduction and a fill over 4 GiB, and an 8192^3 bf16 matmul.
+    Rates are per second of device time between events around `reps` repetitions."""
+    n = 1 << 30  # fp32 elements: 4 GiB
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    out = torch.empty((), device="cuda")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / 1e3 / reps
+
+    nb = 4 * n
+    rows = torch.empty(n // 4096, device="cuda")
+    # the faster of two kernels each for the copy and the read-only stream
+    copy_s = min(timed(lambda: dst.copy_(src)), timed(lambda: torch.mul(src, 1.0, out=dst)))
+    read_s = min(timed(lambda: torch.sum(src, 0, out=out)),
+                 timed(lambda: torch.sum(src.view(-1, 4096), 1, out=rows)))
+    write_s = timed(lambda: dst.fill_(2.0))
+    del rows
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    b = torch.randn((m, m), device="cuda").to(torch.bfloat16)
+    c = torch.empty((m, m), device="cuda", dtype=torch.bfloat16)
+    gemm_s = timed(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {
+        "copy_GBps": 2 * nb / copy_s / 1e9,  # bytes read + written
+        "read_GBps": nb / read_s / 1e9,
+        "write_GBps": nb / write_s / 1e9,
+        "gemm_bf16_TFLOPs": 2.0 * m ** 3 / gemm_s / 1e12,
+        "method": "torch kernels on 4 GiB fp32 (copy: the faster of copy_ and mul by 1; read: the faster of a "
+                  "full sum and a sum of 4096-element rows; write: fill_) and an 8192^3 bf16 matmul, %d "
+                  "repetitions each after 3 untimed" % reps,
+    }
+
+
+def mix_ceiling(ceil, read_bytes, write_bytes):
+    """Rate of a stream with these read and write bytes if its reads ran at the measured
+    read-only rate and its writes at the measured write-only rate, one after the other."""
+    t = read_bytes / ceil["read_GBps"] + write_bytes / ceil["write_GBps"]
+    return (read_bytes + write_bytes) / t
+
+
 def cpu_baseline(wl, torch):
     """The FP64 oracle on this host's cores, on a sample of the prefill workload."""
     import oracle
@@ -478,6 +535,17 @@ def main():
                           "call_ms": o_call, "hbm_frac": ob / (o_call / 1e3) / 1e9 / HBM_PEAK_GBS,
                           "mfma_frac": of / (o_call / 1e3) / 1e12 / BF16_PEAK_TFLOPS})
         out["other"] = other
+    if not args.no_extra:
+        ceil = measured_ceilings(torch)
+        out["measured_ceilings"] = ceil
+        # the prefill moves its algorithmic bytes as reads of Q, K, V (+ state) and writes of Y (+ state)
+        pr = cfg.B * cfg.H * (cfg.T * 768 + STATE_BYTES)
+        pw = cfg.B * cfg.H * (cfg.T * 256 + STATE_BYTES)
+        m = mix_ceiling(ceil, pr, pw)
+        out["roofline"]["measured_ceiling_GBps"] = m
+        out["roofline"]["frac_of_measured"] = achieved / m
+        out["decode"]["roofline"]["measured_ceiling_GBps"] = ceil["copy_GBps"]
+        out["decode"]["roofline"]["frac_of_measured"] = out["decode"]["roofline"]["achieved"] / ceil["copy_GBps"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, torch)
     print(json.dumps(out), flush=True)
