@@ -32,3 +32,13 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_mix_ceiling():
+    # reads at the read rate and writes at the write rate, one after the other
+    ceil = {"read_GBps": 6000.0, "write_GBps": 7000.0}
+    r, w = 3e9, 1e9
+    t = r / 6000.0 + w / 7000.0
+    assert abs(bench.mix_ceiling(ceil, r, w) - (r + w) / t) < 1e-9
+    assert abs(bench.mix_ceiling(ceil, r, 0.0) - 6000.0) < 1e-9
+    assert abs(bench.mix_ceiling(ceil, 0.0, w) - 7000.0) < 1e-9
