@@ -161,6 +161,38 @@ __device__ __forceinline__ float write_weight(const float *lg, const int *zp, in
     return j >= n ? 0.f : w;
 }
 
+// Inclusive scans over the 64 lanes of a wave with data-parallel moves (DPP): shifts by 1,
+// 2, 4 and 8 lanes inside each row of 16, then the row totals carried from lane 15 to rows
+// 1 and 3 and from lane 31 to rows 2 and 3.  A lane whose source falls outside its row, or
+// whose row is masked off, receives the identity.  Full-rate VALU moves, no LDS round trip.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move(int identity, int v)
+{
+    return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ float wave_scan_add(float x)
+{
+    const auto step = [](float v, int moved) { return v + __builtin_bit_cast(float, moved); };
+    const auto bits = [](float v) { return __builtin_bit_cast(int, v); };
+    x = step(x, dpp_move<0x111, 0xf>(0, bits(x)));  // row_shr:1
+    x = step(x, dpp_move<0x112, 0xf>(0, bits(x)));  // row_shr:2
+    x = step(x, dpp_move<0x114, 0xf>(0, bits(x)));  // row_shr:4
+    x = step(x, dpp_move<0x118, 0xf>(0, bits(x)));  // row_shr:8
+    x = step(x, dpp_move<0x142, 0xa>(0, bits(x)));  // row_bcast:15
+    x = step(x, dpp_move<0x143, 0xc>(0, bits(x)));  // row_bcast:31
+    return x;
+}
+__device__ __forceinline__ int wave_scan_max(int x)  // identity -1
+{
+    x = max(x, dpp_move<0x111, 0xf>(-1, x));
+    x = max(x, dpp_move<0x112, 0xf>(-1, x));
+    x = max(x, dpp_move<0x114, 0xf>(-1, x));
+    x = max(x, dpp_move<0x118, 0xf>(-1, x));
+    x = max(x, dpp_move<0x142, 0xa>(-1, x));
+    x = max(x, dpp_move<0x143, 0xc>(-1, x));
+    return x;
+}
+
 template <int C>
 struct Cfg {
     static constexpr int NTJ = C / 16;                 // 16-token tiles per chunk
@@ -322,6 +354,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
                 const float av = j < n ? araw[h] : 1.f;
                 float s = av > 0.f ? __logf(av) : 0.f;
                 int zf = av == 0.f ? j : -1;
+                // (shuffles here: the DPP scans of the chunk-64 passes measured slower in this kernel)
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {
                     const float s2 = __shfl_up(s, off, 64);
@@ -761,15 +794,8 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 const float av = lane < n ? ar : 1.f;
                 float s = av > 0.f ? __logf(av) : 0.f;
                 int zf = av == 0.f ? lane : -1;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float s2 = __shfl_up(s, off, 64);
-                    const int z2 = __shfl_up(zf, off, 64);
-                    if (lane >= off) {
-                        s += s2;
-                        zf = max(zf, z2);
-                    }
-                }
+                s = wave_scan_add(s);
+                zf = wave_scan_max(zf);
                 sm.lg[gs][lane] = s;
                 sm.zp[gs][lane] = zf;
                 sm.gj[gs][lane] = zf >= 0 ? 0.f : __expf(s);
@@ -1158,15 +1184,8 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                 const float av = lane < n ? arx : 1.f;
                 float s = av > 0.f ? __logf(av) : 0.f;
                 int zf = av == 0.f ? lane : -1;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float s2 = __shfl_up(s, off, 64);
-                    const int z2 = __shfl_up(zf, off, 64);
-                    if (lane >= off) {
-                        s += s2;
-                        zf = max(zf, z2);
-                    }
-                }
+                s = wave_scan_add(s);
+                zf = wave_scan_max(zf);
                 sm.lg[gs][lane] = s;
                 sm.zp[gs][lane] = zf;
                 sm.gj[gs][lane] = zf >= 0 ? 0.f : __expf(s);
