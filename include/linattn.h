@@ -120,7 +120,11 @@ la_status la_state_init(void *S, void *z, int64_t n_states, int32_t r, int32_t d
  *   chunk  tokens per chunk, 1..128 (the last chunk of a sequence may be shorter)
  * bf16 io with d = dv = 128 and chunk 64 or 128 runs on bf16 MFMA with fp32
  * accumulation and fp32 state; every other valid request runs a general kernel
- * that computes in the state dtype.
+ * that computes in the state dtype.  The bf16 path splits long sequences into
+ * segments and keeps each segment's state (66,064 bytes) in that segment's rows of
+ * Y until they are overwritten with its outputs, so Y is working memory for the
+ * duration of the call: its contents are defined only once the call's work on
+ * `stream` has finished.  No other memory is used.
  * Errors: LA_ERR_NULL, LA_ERR_SHAPE (B, H, T, d, dv < 1), LA_ERR_DTYPE, LA_ERR_EPS,
  * LA_ERR_CHUNK, LA_ERR_UNSUPPORTED (d or dv > 128, chunk > 128), LA_ERR_ALIAS,
  * LA_ERR_LAUNCH.
