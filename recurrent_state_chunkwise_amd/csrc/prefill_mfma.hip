@@ -48,7 +48,6 @@ typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;          // feature width d = r and value width dv
-constexpr int kThreads = 512;    // 8 waves
 constexpr float kLog2e = 1.4426950408889634f;
 
 // (sequence, segment) workgroups aimed for, per chunk size: one or two per compute unit
@@ -197,45 +196,8 @@ template <int C>
 struct Cfg {
     static constexpr int NTJ = C / 16;                 // 16-token tiles per chunk
     static constexpr int NKI = C / 32;                 // 32-token MFMA steps per chunk
-    static constexpr int TPT = C / 32;                 // tokens per staging thread
     static constexpr int NPT = NTJ * (NTJ + 1) / 2;    // tiles on or below the diagonal
 };
-
-// LDS.  Row-major tiles (Qs, Ks) hold 128 features per token; the token-major tiles
-// (KwT: features x tokens, VT: values x tokens) are the K-contiguous operands of the
-// contractions over tokens.  16-byte granules are XOR-swizzled per row so that the
-// 16 rows read by one MFMA operand land in distinct banks.
-template <int C>
-struct alignas(16) Smem {
-    typedef Cfg<C> G;
-    static constexpr int QN = C * kD;
-    static constexpr int PN = G::NPT;
-    alignas(16) bf16 Qs[QN];         // phi(q) rows
-    alignas(16) bf16 Ks[QN];         // phi(k) rows
-    alignas(16) bf16 KwT[kD * C];    // w phi(k), token-major
-    alignas(16) bf16 VT[kD * C];     // values, token-major
-    alignas(16) uint2 P[PN * 64];    // bf16 score tiles, one 4-value group per lane
-    alignas(16) float zs[2][kD];     // z entering the chunk, by chunk parity
-    alignas(16) float lg[2][C];      // in-chunk prefix sum of log(alpha) (0 at zero gates)
-    alignas(16) float gj[2][C];      // product of the chunk's gates up to j
-    alignas(16) int zp[2][C];        // last zero gate at or before j, -1 if none
-};
-
-// swizzled element offsets
-__device__ __forceinline__ int qk_off(int row, int col)  // [C][128]
-{
-    return row * kD + ((((col >> 3) ^ (row & 15)) << 3) | (col & 7));
-}
-template <int C>
-__device__ __forceinline__ int tm_off(int row, int tok)  // [128][C]
-{
-    int h;
-    if constexpr (C == 128)
-        h = (row + (row >> 4)) & 15;
-    else
-        h = (row >> 1) & 7;
-    return row * C + ((((tok >> 3) ^ h) << 3) | (tok & 7));
-}
 
 struct Args {
     const bf16 *Q, *K, *V;
@@ -251,381 +213,6 @@ struct Args {
 __device__ __forceinline__ float *slot_ptr(const Args &a, int64_t head, int p)
 {
     return reinterpret_cast<float *>(a.Y + (head * a.T + (int64_t)p * a.seg_len) * kD);
-}
-
-// Pass 3 with 8 waves that stage and multiply in turn (the form used at chunk 128,
-// where two buffers of every tile do not fit in LDS): outputs from the entering state;
-// the last segment writes S, z.
-template <int C, bool GATED, int FM>
-__global__ __launch_bounds__(kThreads) void chunk_kernel(Args a)
-{
-    typedef Cfg<C> G;
-    __shared__ Smem<C> sm;
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int lr = lane & 15;   // row / column inside a 16x16 tile
-    const int lg4 = lane >> 4;  // lane group
-
-    const int64_t head = blockIdx.x / a.nseg;
-    const int seg = blockIdx.x % a.nseg;
-    const int64_t s0 = (int64_t)seg * a.seg_len;
-    const int64_t s1 = seg == a.nseg - 1 ? a.T : s0 + a.seg_len;
-    const int64_t len = s1 - s0;
-    const int n_chunks = (int)((len + C - 1) / C);
-    auto chunk_len = [&](int c) { return (int)min((int64_t)C, len - (int64_t)c * C); };
-
-    // this segment's rows of Q, K, V, Y (256 bytes per token) and of alpha (4 bytes)
-    const int64_t row0 = head * a.T + s0;
-    const rsrc_t rQ = make_rsrc(a.Q + row0 * kD, len * kD * 2);
-    const rsrc_t rK = make_rsrc(a.K + row0 * kD, len * kD * 2);
-    const rsrc_t rV = make_rsrc(a.V + row0 * kD, len * kD * 2);
-    const rsrc_t rY = make_rsrc(a.Y + row0 * kD, len * kD * 2);
-    const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
-
-    bf16x8 ones;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-        ones[s] = static_cast<bf16>(1.f);
-
-    // ---------------------------------------------------------------- entering state
-    // wave w owns value columns c = 16w + lr of S (tile tf holds rows f = 16tf + 4lg4 + r)
-    // and features f = 16w + 4lg4 + r of z
-    f32x4 sacc[8];
-    f32x4 zr;
-    const int cw = wave * 16 + lr;
-    const int fw = wave * 16 + lg4 * 4;
-    {
-        const float *Sin = a.nseg == 1 ? a.S + head * kD * kD : slot_ptr(a, head, seg);
-        const float *zin = a.nseg == 1 ? a.z + head * kD : Sin + kD * kD;
-#pragma unroll
-        for (int tf = 0; tf < 8; ++tf)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sacc[tf][r] = Sin[(tf * 16 + lg4 * 4 + r) * kD + cw];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            zr[r] = zin[fw + r];
-        if (tid < kD)
-            sm.zs[0][tid] = zin[tid];
-    }
-
-    // ---------------------------------------------------------------- loads
-    // every thread stages TPT consecutive tokens of one 8-wide granule of Q, K and V:
-    // thread (fg, tg) holds granule fg of tokens tg*TPT .. tg*TPT + TPT - 1
-    const int fg = tid & 15, tg = tid >> 4;
-    uint4 raw_q[G::TPT], raw_k[G::TPT], raw_v[G::TPT];
-    float araw[C / 64];
-    const int ld_off = (tg * G::TPT) * kD * 2 + fg * 16;  // byte offset of this thread's first row
-
-    auto prefetch_k = [&](int chunk) {
-        const int off = chunk * C * kD * 2 + ld_off;
-#pragma unroll
-        for (int p = 0; p < G::TPT; ++p)
-            raw_k[p] = bload16<kNT>(rK, off + p * kD * 2);
-    };
-    auto prefetch_qv = [&](int chunk) {
-        const int off = chunk * C * kD * 2 + ld_off;
-#pragma unroll
-        for (int p = 0; p < G::TPT; ++p) {
-            raw_q[p] = bload16<kNT>(rQ, off + p * kD * 2);
-            raw_v[p] = bload16<kNT>(rV, off + p * kD * 2);
-        }
-    };
-    auto prefetch_a = [&](int chunk) {
-        if (GATED && wave == 0) {
-#pragma unroll
-            for (int h = 0; h < C / 64; ++h)
-                araw[h] = __uint_as_float(
-                    (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (chunk * C + h * 64 + lane) * 4, 0, kNT));
-        }
-    };
-
-    // ---------------------------------------------------------------- gates
-    // wave 0: inclusive scans of log(alpha) and of the last zero-gate position
-    auto gate_scan = [&](int n, int gs) {
-        if (GATED && wave == 0) {
-            float carry = 0.f;
-            int zcarry = -1;
-#pragma unroll
-            for (int h = 0; h < C / 64; ++h) {
-                const int j = h * 64 + lane;
-                const float av = j < n ? araw[h] : 1.f;
-                float s = av > 0.f ? __logf(av) : 0.f;
-                int zf = av == 0.f ? j : -1;
-                // (shuffles here: the DPP scans of the chunk-64 passes measured slower in this kernel)
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float s2 = __shfl_up(s, off, 64);
-                    const int z2 = __shfl_up(zf, off, 64);
-                    if (lane >= off) {
-                        s += s2;
-                        zf = max(zf, z2);
-                    }
-                }
-                s += carry;
-                zf = max(zf, zcarry);
-                sm.lg[gs][j] = s;
-                sm.zp[gs][j] = zf;
-                sm.gj[gs][j] = zf >= 0 ? 0.f : __expf(s);
-                carry = __shfl(s, 63, 64);
-                zcarry = __shfl(zf, 63, 64);
-            }
-        }
-    };
-    // ---------------------------------------------------------------- staging
-    // keys: phi, row-major K~ for the scores and the token-major write weights
-    // w_j phi(k_j) (w_j = gates after j to the chunk end, 0 past the end of the segment,
-    // whose tokens load as zeros); values: token-major V.
-    auto stage_k = [&](int n, int gs) {
-        unsigned kwp[G::TPT][4];  // bf16 pairs of w*phi(k)
-#pragma unroll
-        for (int p = 0; p < G::TPT; ++p) {
-            const int j = tg * G::TPT + p;
-            const float w = write_weight<GATED>(sm.lg[gs], sm.zp[gs], n, j);
-            float x[8];
-            unpack8(raw_k[p], x);
-            bf16x8 kb;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const float f = phi<FM>(x[s]);
-                kb[s] = static_cast<bf16>(f);
-                if (GATED)
-                    x[s] = w * f;
-            }
-            *reinterpret_cast<bf16x8 *>(&sm.Ks[qk_off(j, fg * 8)]) = kb;
-            uint4 u;
-            if (GATED) {
-                bf16x8 kwb;
-#pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    kwb[s] = static_cast<bf16>(x[s]);
-                u = *reinterpret_cast<uint4 *>(&kwb);
-            } else {
-                u = j < n ? *reinterpret_cast<uint4 *>(&kb) : make_uint4(0u, 0u, 0u, 0u);
-            }
-            kwp[p][0] = u.x, kwp[p][1] = u.y, kwp[p][2] = u.z, kwp[p][3] = u.w;
-        }
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int row = fg * 8 + s;
-            unsigned o[G::TPT / 2];
-#pragma unroll
-            for (int q = 0; q < G::TPT / 2; ++q)
-                o[q] = (s & 1) ? pack_hi(kwp[2 * q][s >> 1], kwp[2 * q + 1][s >> 1])
-                               : pack_lo(kwp[2 * q][s >> 1], kwp[2 * q + 1][s >> 1]);
-            if constexpr (G::TPT == 2)
-                *reinterpret_cast<unsigned *>(&sm.KwT[tm_off<C>(row, tg * 2)]) = o[0];
-            else
-                *reinterpret_cast<uint2 *>(&sm.KwT[tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
-        }
-    };
-    auto stage_q = [&]() {
-#pragma unroll
-        for (int p = 0; p < G::TPT; ++p) {
-            const int j = tg * G::TPT + p;
-            float x[8];
-            unpack8(raw_q[p], x);
-            bf16x8 qb;
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                qb[s] = static_cast<bf16>(phi<FM>(x[s]));
-            *reinterpret_cast<bf16x8 *>(&sm.Qs[qk_off(j, fg * 8)]) = qb;
-        }
-    };
-    // value column 8fg+s gets this thread's TPT tokens
-    auto stage_v = [&]() {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int row = fg * 8 + s;
-            unsigned o[G::TPT / 2];
-#pragma unroll
-            for (int q = 0; q < G::TPT / 2; ++q) {
-                const unsigned lo = (&raw_v[2 * q].x)[s >> 1], hi = (&raw_v[2 * q + 1].x)[s >> 1];
-                o[q] = (s & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
-            }
-            if constexpr (G::TPT == 2)
-                *reinterpret_cast<unsigned *>(&sm.VT[tm_off<C>(row, tg * 2)]) = o[0];
-            else
-                *reinterpret_cast<uint2 *>(&sm.VT[tm_off<C>(row, tg * 4)]) = make_uint2(o[0], o[1]);
-        }
-    };
-
-    // ---------------------------------------------------------------- chunk products
-    // (1) score tiles on or below the diagonal, distributed over the waves.  The tile
-    // is K~ Q~^T, so lane (lr, lg4) holds scores (j = 16tj + lr, i = 16ti + 4lg4 + r),
-    // masked to i <= j and weighted by the gates of tokens i+1..j.
-    auto scores = [&](int gs) {
-        for (int k = wave; k < G::NPT; k += 8) {
-            int tj = 0;
-            while ((tj + 1) * (tj + 2) / 2 <= k)
-                ++tj;
-            const int ti = k - tj * (tj + 1) / 2;
-            const int j = tj * 16 + lr;
-            int ii[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                ii[r] = ti * 16 + lg4 * 4 + r;
-            float dec[4];
-            pair_decays<GATED>(sm.lg[gs], sm.zp[gs], j, ii, dec);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kf = 0; kf < 4; ++kf) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&sm.Ks[qk_off(ti * 16 + lr, kf * 32 + lg4 * 8)]);
-                const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&sm.Qs[qk_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
-                acc = mfma(ka, qb, acc);
-            }
-            bf16x4 pk;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                pk[r] = static_cast<bf16>(ii[r] <= j ? acc[r] * dec[r] : 0.f);
-            sm.P[k * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
-        }
-    };
-    // (2) + (3) for this wave's 16 value columns, computed transposed:
-    //   N^T = S_prev^T Q~^T (gated by g_j) + V^T P^T,   D = z_prev^T Q~^T (gated) + 1^T P^T
-    // Accumulator lane (lr, lg4) holds token j = 16tj + lr, columns fw .. fw + 3, and the
-    // denominator of token j, so each lane writes 8 contiguous bytes of y.  Operands of
-    // one K step are two 16-row tiles: rows 4lg4..4lg4+3 of each give the permuted k
-    // order, used alike on both sides of every product.
-    auto outputs = [&](int gs, int64_t t0, int zbuf) {
-        bf16x8 sb[4], zb[4];
-#pragma unroll
-        for (int kf = 0; kf < 4; ++kf) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sb[kf][r] = static_cast<bf16>(sacc[2 * kf][r]);
-                sb[kf][4 + r] = static_cast<bf16>(sacc[2 * kf + 1][r]);
-            }
-            const f32x4 zlo = *reinterpret_cast<const f32x4 *>(&sm.zs[zbuf][kf * 32 + lg4 * 4]);
-            const f32x4 zhi = *reinterpret_cast<const f32x4 *>(&sm.zs[zbuf][kf * 32 + 16 + lg4 * 4]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                zb[kf][r] = static_cast<bf16>(zlo[r]);
-                zb[kf][4 + r] = static_cast<bf16>(zhi[r]);
-            }
-        }
-        // two token tiles per iteration: their chains overlap (unrolling further spills)
-#pragma unroll 2
-        for (int tj = 0; tj < G::NTJ; ++tj) {
-            const int j = tj * 16 + lr;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, dac = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kf = 0; kf < 4; ++kf) {
-                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&sm.Qs[qk_off(j, kf * 32 + lg4 * 4)]);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&sm.Qs[qk_off(j, kf * 32 + 16 + lg4 * 4)]);
-                const bf16x8 qb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                acc = mfma(sb[kf], qb, acc);
-                dac = mfma(zb[kf], qb, dac);
-            }
-            if (GATED) {
-                const float g = sm.gj[gs][j];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[r] *= g;
-                dac[0] *= g;  // only element 0 of the denominator is read
-            }
-            for (int ki = 0; 2 * ki <= tj; ++ki) {
-                const int k1 = tj * (tj + 1) / 2 + 2 * ki;
-                const uint2 p1 = sm.P[k1 * 64 + lane];
-                const uint2 p2 = 2 * ki + 1 <= tj ? sm.P[(k1 + 1) * 64 + lane] : make_uint2(0u, 0u);
-                const bf16x4 a1 = *reinterpret_cast<const bf16x4 *>(&p1);
-                const bf16x4 a2 = *reinterpret_cast<const bf16x4 *>(&p2);
-                const bf16x8 pb = {a1[0], a1[1], a1[2], a1[3], a2[0], a2[1], a2[2], a2[3]};
-                const bf16x4 vlo = *reinterpret_cast<const bf16x4 *>(&sm.VT[tm_off<C>(cw, ki * 32 + lg4 * 4)]);
-                const bf16x4 vhi = *reinterpret_cast<const bf16x4 *>(&sm.VT[tm_off<C>(cw, ki * 32 + 16 + lg4 * 4)]);
-                const bf16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
-                acc = mfma(va, pb, acc);
-                dac = mfma(ones, pb, dac);
-            }
-            const float inv = __builtin_amdgcn_rcpf(dac[0] + a.eps);
-            bf16x4 yb;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                yb[r] = static_cast<bf16>(acc[r] * inv);
-            // rows past the end of the segment fall outside rY and are dropped
-            const int off = (int)((t0 + j) * kD + fw) * 2;
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, yb),
-                                                  rY, off, 0, kNT);
-        }
-    };
-    // (4) S = g_end S + (w K~)^T V for this wave's columns, and
-    //     z = g_end z + (w K~)^T 1 for this wave's features (published for the next chunk)
-    auto state_write = [&](float g_end, int znext) {
-        if (GATED) {
-#pragma unroll
-            for (int tf = 0; tf < 8; ++tf)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sacc[tf][r] *= g_end;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                zr[r] *= g_end;
-        }
-#pragma unroll
-        for (int ki = 0; ki < G::NKI; ++ki) {
-            const bf16x8 vb = *reinterpret_cast<const bf16x8 *>(&sm.VT[tm_off<C>(cw, ki * 32 + lg4 * 8)]);
-#pragma unroll
-            for (int tf = 0; tf < 8; ++tf) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&sm.KwT[tm_off<C>(tf * 16 + lr, ki * 32 + lg4 * 8)]);
-                sacc[tf] = mfma(ka, vb, sacc[tf]);
-            }
-            const bf16x8 kz = *reinterpret_cast<const bf16x8 *>(&sm.KwT[tm_off<C>(wave * 16 + lr, ki * 32 + lg4 * 8)]);
-            zr = mfma(kz, ones, zr);
-        }
-        if (lr == 0)
-            *reinterpret_cast<f32x4 *>(&sm.zs[znext][fw]) = zr;
-    };
-
-    // ---------------------------------------------------------------- walk: stage, then multiply
-    prefetch_k(0);
-    prefetch_qv(0);
-    prefetch_a(0);
-    gate_scan(chunk_len(0), 0);
-    __syncthreads();
-
-    for (int c = 0; c < n_chunks; ++c) {
-        const int64_t t0 = (int64_t)c * C;
-        const int n = chunk_len(c);
-        const int gs = c & 1;
-        const bool more = c + 1 < n_chunks;
-
-        stage_k(n, gs);
-        stage_q();
-        stage_v();
-        if (more) {
-            prefetch_k(c + 1);
-            prefetch_qv(c + 1);
-            prefetch_a(c + 1);
-        }
-        __syncthreads();  // A: chunk staged
-
-        scores(gs);
-        __syncthreads();  // B: score tiles ready
-        outputs(gs, t0, c & 1);
-        const float g_end = GATED ? sm.gj[gs][n - 1] : 1.f;
-        state_write(g_end, (c + 1) & 1);
-        if (more)
-            gate_scan(chunk_len(c + 1), gs ^ 1);
-        __syncthreads();  // C: chunk done
-    }
-
-    // ---------------------------------------------------------------- leaving state
-    if (seg != a.nseg - 1)
-        return;
-    float *Sout = a.S + head * kD * kD;
-    float *zout = a.z + head * kD;
-#pragma unroll
-    for (int tf = 0; tf < 8; ++tf)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Sout[(tf * 16 + lg4 * 4 + r) * kD + cw] = sacc[tf][r];
-    if (lr == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            zout[fw + r] = zr[r];
-    }
 }
 
 // ============================================================================ pass 3, chunk 64
@@ -1106,6 +693,392 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
     }
 }
 
+// ============================================================================ pass 3, chunk 128
+// Producer / consumer form at chunk 128.  Two buffers of every 128-token tile do not fit
+// in LDS, so each tile has one buffer and the producers stage it in the half of the chunk
+// in which the consumers do not read it:
+//   part A (consumers: (2), phi(q).z_prev, scores (1); read Q~, K~)  producers stage V and
+//          the write weights of this chunk;
+//   part B (consumers: (3), outputs, (4); read V, the write weights, the score tiles)
+//          producers scan the gates of the next chunk and stage its Q~ and K~.
+// Q and V registers are refilled right after they are staged, so those loads have a whole
+// chunk to arrive.  The raw K rows stay in registers from the staging of K~ to that of the
+// write weights, so w phi(k) is formed in fp32 and rounded once, as in the chunk-64 form;
+// K is then loaded for the next chunk, with the compute of part A to arrive.
+// y leaves straight from the consumers, 8 bytes per lane.
+constexpr int kP8C = 128;
+constexpr int kP8Producers = 4;
+constexpr int kP8Threads = kPcConsumers + 64 * kP8Producers;
+
+struct alignas(16) P8Smem {
+    alignas(16) bf16 Qs[kP8C * kRow];  // phi(q)
+    alignas(16) bf16 Ks[kP8C * kRow];  // phi(k), rows of the scores
+    alignas(16) bf16 Vs[kP8C * kRow];  // v
+    alignas(16) bf16 Kw[kP8C * kRow];  // write weights w phi(k), 0 past the end of the segment
+    alignas(16) uint2 P[Cfg<kP8C>::NPT * 64];  // bf16 score tile (tj, ti) at tj (tj + 1) / 2 + ti
+    alignas(16) float zs[2][kD];       // z entering the chunk, by chunk parity
+    alignas(16) float dq[kP8C];        // phi(q_j) . z_prev
+    alignas(16) float lg[2][kP8C];
+    alignas(16) float gj[2][kP8C];
+    alignas(16) int zp[2][kP8C];
+};
+static_assert(sizeof(P8Smem) <= 160 * 1024, "the chunk-128 tiles must fit in the 160 KB of LDS");
+
+template <bool GATED, int FM>
+__global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
+{
+    constexpr int C = kP8C;
+    typedef Cfg<C> G;
+    static_assert(G::NTJ == 8 && G::NKI == 4, "8 token tiles, one per consumer wave");
+    __shared__ P8Smem sm;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int lr = lane & 15;
+    const int lg4 = lane >> 4;
+
+    const int64_t head = blockIdx.x / a.nseg;
+    const int seg = blockIdx.x % a.nseg;
+    const int64_t s0 = (int64_t)seg * a.seg_len;
+    const int64_t s1 = seg == a.nseg - 1 ? a.T : s0 + a.seg_len;
+    const int64_t len = s1 - s0;
+    const int n_chunks = (int)((len + C - 1) / C);
+    auto chunk_len = [&](int c) { return (int)min((int64_t)C, len - (int64_t)c * C); };
+    const int64_t row0 = head * a.T + s0;
+
+    if (wave >= 8) {
+        // ============================================================ producers
+        const rsrc_t rQ = make_rsrc(a.Q + row0 * kD, len * kD * 2);
+        const rsrc_t rK = make_rsrc(a.K + row0 * kD, len * kD * 2);
+        const rsrc_t rV = make_rsrc(a.V + row0 * kD, len * kD * 2);
+        const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
+        const int pt = tid - kPcConsumers;
+        const bool scanner = wave == 8;
+        // thread (fg, tg) stages granule fg (8 features) of tokens TPT tg .. TPT tg + TPT - 1
+        constexpr int TPT = C / 16;
+        const int fg = pt & 15, tg = pt >> 4;
+        const int ld_off = tg * TPT * kD * 2 + fg * 16;
+        uint4 rq[TPT], rk[TPT], rv[TPT];
+        float ar[2] = {0.f, 0.f};  // alpha of the next chunk to scan: tokens lane, 64 + lane
+
+        auto load = [&](const rsrc_t &r, int c, uint4 (&x)[TPT]) {
+#pragma unroll
+            for (int p = 0; p < TPT; ++p)
+                x[p] = bload16<kNT>(r, c * C * kD * 2 + ld_off + p * kD * 2);
+        };
+        auto load_a = [&](int c) {
+            if (GATED) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    ar[h] = __uint_as_float(
+                        (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (c * C + h * 64 + lane) * 4, 0, kNT));
+            }
+        };
+        // inclusive scans of log(alpha) and of the last zero-gate position over the chunk
+        auto scan = [&](int n, int gs) {
+            if (GATED && scanner) {
+                float carry = 0.f;
+                int zcarry = -1;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int j = h * 64 + lane;
+                    const float av = j < n ? ar[h] : 1.f;
+                    float sv = av > 0.f ? __logf(av) : 0.f;
+                    int zf = av == 0.f ? j : -1;
+                    sv = wave_scan_add(sv) + carry;
+                    zf = max(wave_scan_max(zf), zcarry);
+                    sm.lg[gs][j] = sv;
+                    sm.zp[gs][j] = zf;
+                    sm.gj[gs][j] = zf >= 0 ? 0.f : __expf(sv);
+                    carry = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv), 63));
+                    zcarry = __builtin_amdgcn_readlane(zf, 63);
+                }
+            }
+        };
+        // phi(q) and phi(k) rows
+        auto stage_qk = [&]() {
+#pragma unroll
+            for (int p = 0; p < TPT; ++p) {
+                const int j = tg * TPT + p;
+                float x[8];
+                unpack8(rq[p], x);
+                bf16x8 qb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    qb[e] = static_cast<bf16>(phi<FM>(x[e]));
+                *reinterpret_cast<bf16x8 *>(&sm.Qs[pr_off(j, fg * 8)]) = qb;
+                unpack8(rk[p], x);
+                bf16x8 kb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    kb[e] = static_cast<bf16>(phi<FM>(x[e]));
+                *reinterpret_cast<bf16x8 *>(&sm.Ks[pr_off(j, fg * 8)]) = kb;
+            }
+        };
+        // V rows and the write weights w_j phi(k_j) (w_j = gates after j to the chunk end,
+        // 0 past the end of the segment)
+        auto stage_vw = [&](int gs, int n) {
+#pragma unroll
+            for (int p = 0; p < TPT; ++p) {
+                const int j = tg * TPT + p;
+                *reinterpret_cast<uint4 *>(&sm.Vs[pr_off(j, fg * 8)]) = rv[p];
+                const float w = write_weight<GATED>(sm.lg[gs], sm.zp[gs], n, j);
+                float x[8];
+                unpack8(rk[p], x);
+                bf16x8 kwb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    kwb[e] = static_cast<bf16>(w * phi<FM>(x[e]));
+                *reinterpret_cast<bf16x8 *>(&sm.Kw[pr_off(j, fg * 8)]) = kwb;
+            }
+        };
+
+        // prologue: chunk 0's Q~ and K~ staged, its gates scanned; chunk 1's Q in flight
+        load(rQ, 0, rq);
+        load(rK, 0, rk);
+        load(rV, 0, rv);
+        load_a(0);
+        scan(chunk_len(0), 0);
+        load_a(1);
+        stage_qk();
+        load(rQ, 1, rq);
+        wg_barrier();
+        // Loads past the end of the segment read zeros through the buffer resources; they
+        // are issued unconditionally so that every wait on them is a counted one.
+        for (int c = 0; c < n_chunks; ++c) {
+            // part A of chunk c
+            stage_vw(c & 1, chunk_len(c));
+            load(rV, c + 1, rv);
+            load(rK, c + 1, rk);
+            wg_barrier();  // a | b
+            // part B of chunk c
+            if (c + 1 < n_chunks)
+                scan(chunk_len(c + 1), (c + 1) & 1);
+            load_a(c + 2);
+            stage_qk();
+            load(rQ, c + 2, rq);
+            wg_barrier();  // chunk c done
+        }
+        return;
+    }
+
+    // ================================================================ consumers
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        ones[e] = static_cast<bf16>(1.f);
+    f32x4 sacc[8];
+    f32x4 zr;
+    const int cw = wave * 16 + lr;
+    const int fw = wave * 16 + lg4 * 4;
+    {
+        const float *Sin = a.nseg == 1 ? a.S + head * kD * kD : slot_ptr(a, head, seg);
+        const float *zin = a.nseg == 1 ? a.z + head * kD : Sin + kD * kD;
+#pragma unroll
+        for (int tf = 0; tf < 8; ++tf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sacc[tf][r] = Sin[(tf * 16 + lg4 * 4 + r) * kD + cw];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zr[r] = zin[fw + r];
+        if (tid < kD)
+            sm.zs[0][tid] = zin[tid];
+    }
+    const rsrc_t rY = make_rsrc(a.Y + row0 * kD, len * kD * 2);
+    // transposing-load addresses: this lane supplies 4 adjacent columns (4 (lr & 3) ..)
+    // of token row e = lr >> 2 of its group's set
+    const int te = lr >> 2, tc = 4 * (lr & 3);
+    wg_barrier();
+
+    for (int c = 0; c < n_chunks; ++c) {
+        const int buf = c & 1;
+        const int n = chunk_len(c);
+
+        // ---- part A: (2) for the eight token tiles, phi(q) . z_prev for tile `wave`, scores
+        f32x4 acc[G::NTJ];
+#pragma unroll
+        for (int tj = 0; tj < G::NTJ; ++tj)
+            acc[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kf = 0; kf < 4; ++kf) {
+            // K step kf: feature tiles 2kf and 2kf+1 of S_prev in bf16; their accumulator
+            // rows 4lg4..4lg4+3 give the permuted k order used on both sides
+            bf16x8 sb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sb[r] = static_cast<bf16>(sacc[2 * kf][r]);
+                sb[4 + r] = static_cast<bf16>(sacc[2 * kf + 1][r]);
+            }
+            const int hi_col = opaque(kf * 32 + 16 + lg4 * 4);
+#pragma unroll
+            for (int tj = 0; tj < G::NTJ; ++tj) {
+                const int j = tj * 16 + lr;
+                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&sm.Qs[pr_off(j, kf * 32 + lg4 * 4)]);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&sm.Qs[pr_off(j, hi_col)]);
+                acc[tj] = mfma(sb, cat8(lo, hi), acc[tj]);
+            }
+        }
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        {
+            const int j = wave * 16 + lr;
+#pragma unroll
+            for (int kf = 0; kf < 4; ++kf) {
+                const f32x4 zlo = *reinterpret_cast<const f32x4 *>(&sm.zs[buf][kf * 32 + lg4 * 4]);
+                const f32x4 zhi = *reinterpret_cast<const f32x4 *>(&sm.zs[buf][kf * 32 + 16 + lg4 * 4]);
+                bf16x8 zb;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    zb[r] = static_cast<bf16>(zlo[r]);
+                    zb[4 + r] = static_cast<bf16>(zhi[r]);
+                }
+                const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&sm.Qs[pr_off(j, kf * 32 + lg4 * 4)]);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&sm.Qs[pr_off(j, opaque(kf * 32 + 16 + lg4 * 4))]);
+                d = mfma(zb, cat8(lo, hi), d);
+            }
+        }
+        for (int k = wave; k < G::NPT; k += 8) {
+            int tj = 0;
+            while ((tj + 1) * (tj + 2) / 2 <= k)
+                ++tj;
+            const int ti = k - tj * (tj + 1) / 2;
+            // acc[r] = score (j = 16tj + lr, i = 16ti + sigma(4lg4 + r))
+            const int j = tj * 16 + lr;
+            int ii[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ii[r] = ti * 16 + sigma(lg4 * 4 + r);
+            float dec[4];
+            pair_decays<GATED>(sm.lg[buf], sm.zp[buf], j, ii, dec);
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kf = 0; kf < 4; ++kf) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&sm.Ks[pr_off(ti * 16 + sigma(lr), kf * 32 + lg4 * 8)]);
+                const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&sm.Qs[pr_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
+                sc = mfma(ka, qb, sc);
+            }
+            bf16x4 pk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pk[r] = static_cast<bf16>(ii[r] <= j ? sc[r] * dec[r] : 0.f);
+            sm.P[k * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
+        }
+        if (lg4 == 0)
+            sm.dq[wave * 16 + lr] = d[0];
+        wg_barrier();  // a | b
+
+        // ---- part B: (3) with V^T in the score tiles' k order (tokens sigma(4lg4 + e) and
+        //      16 + sigma(4lg4 + e) of the 32-token step), outputs, then (4)
+        auto out_begin = [&](int tj, f32x4 &dac) {
+            const int j = tj * 16 + lr;
+            dac = f32x4{sm.dq[j], 0.f, 0.f, 0.f};  // only element 0 is read
+            if (GATED) {
+                const float g = sm.gj[buf][j];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[tj][r] *= g;
+                dac[0] *= g;
+            }
+        };
+        auto out_step = [&](int tj, int ki, uint2 p0, uint2 p1, f32x4 &dac) {
+            const bf16x8 pb = cat8(__builtin_bit_cast(bf16x4, p0), __builtin_bit_cast(bf16x4, p1));
+            const int tb = ki * 32 + sigma(lg4 * 4 + te);
+            const bf16x8 va = cat8(ld_tr(&sm.Vs[pr_off(tb, wave * 16 + tc)]), ld_tr(&sm.Vs[pr_off(tb + 16, wave * 16 + tc)]));
+            acc[tj] = mfma(va, pb, acc[tj]);
+            dac = mfma(ones, pb, dac);
+        };
+        auto out_end = [&](int tj, const f32x4 &dac) {
+            const int j = tj * 16 + lr;
+            const float inv = __builtin_amdgcn_rcpf(dac[0] + a.eps);
+            bf16x4 yb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                yb[r] = static_cast<bf16>(acc[tj][r] * inv);
+            // rows past the end of the segment fall outside rY and are dropped
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, yb),
+                                                  rY, ((c * C + j) * kD + fw) * 2, 0, kNT);
+        };
+        if constexpr (GATED) {
+            // token tiles in pairs (2m, 2m + 1): tile 2m has m full pairs of score tiles and
+            // the diagonal tile alone, tile 2m + 1 has m + 1 full pairs, so no score read is
+            // conditional (in the ungated instance this form spills LDS addresses inside the
+            // chunk loop and measured slower than the form below)
+#pragma unroll 1
+            for (int m = 0; m < G::NTJ / 2; ++m) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int tj = 2 * m + h;
+                    const int kbase = tj * (tj + 1) / 2;
+                    f32x4 dac;
+                    out_begin(tj, dac);
+                    for (int ki = 0; ki < m + h; ++ki)
+                        out_step(tj, ki, sm.P[(kbase + 2 * ki) * 64 + lane], sm.P[(kbase + 2 * ki + 1) * 64 + lane], dac);
+                    if (h == 0)
+                        out_step(tj, m, sm.P[(kbase + 2 * m) * 64 + lane], make_uint2(0u, 0u), dac);
+                    out_end(tj, dac);
+                }
+            }
+        } else {
+#pragma unroll 2
+            for (int tj = 0; tj < G::NTJ; ++tj) {
+                const int kbase = tj * (tj + 1) / 2;
+                f32x4 dac;
+                out_begin(tj, dac);
+                for (int ki = 0; 2 * ki <= tj; ++ki) {
+                    const uint2 p0 = sm.P[(kbase + 2 * ki) * 64 + lane];
+                    const uint2 p1 = 2 * ki + 1 <= tj ? sm.P[(kbase + 2 * ki + 1) * 64 + lane] : make_uint2(0u, 0u);
+                    out_step(tj, ki, p0, p1, dac);
+                }
+                out_end(tj, dac);
+            }
+        }
+        const float g_end = GATED ? sm.gj[buf][n - 1] : 1.f;
+        if (GATED) {
+#pragma unroll
+            for (int tf = 0; tf < 8; ++tf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sacc[tf][r] *= g_end;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                zr[r] *= g_end;
+        }
+        // (4) in k order: lane group lg4 takes tokens 8lg4 + 2e (first load) and
+        //     8lg4 + 2e + 1 (second) of each 32-token step, alike for both operands
+#pragma unroll
+        for (int ki = 0; ki < G::NKI; ++ki) {
+            const int tb = ki * 32 + lg4 * 8 + 2 * te;
+            const bf16x8 vb = cat8(ld_tr(&sm.Vs[pr_off(tb, wave * 16 + tc)]), ld_tr(&sm.Vs[pr_off(tb + 1, wave * 16 + tc)]));
+#pragma unroll
+            for (int tf = 0; tf < 8; ++tf) {
+                const bf16x8 ka = cat8(ld_tr(&sm.Kw[pr_off(tb, tf * 16 + tc)]), ld_tr(&sm.Kw[pr_off(tb + 1, tf * 16 + tc)]));
+                sacc[tf] = mfma(ka, vb, sacc[tf]);
+            }
+            const bf16x8 kz = cat8(ld_tr(&sm.Kw[pr_off(tb, wave * 16 + tc)]), ld_tr(&sm.Kw[pr_off(tb + 1, wave * 16 + tc)]));
+            zr = mfma(kz, ones, zr);
+        }
+        if (lr == 0)
+            *reinterpret_cast<f32x4 *>(&sm.zs[buf ^ 1][fw]) = zr;
+        wg_barrier();  // chunk c done
+    }
+
+    if (seg != a.nseg - 1)
+        return;
+    float *Sout = a.S + head * kD * kD;
+    float *zout = a.z + head * kD;
+#pragma unroll
+    for (int tf = 0; tf < 8; ++tf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Sout[(tf * 16 + lg4 * 4 + r) * kD + cw] = sacc[tf][r];
+    if (lr == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zout[fw + r] = zr[r];
+    }
+}
+
 // ============================================================================ pass 1, chunk 64
 // Segment maps in the same producer / consumer form: producers stage the write weights
 // w phi(k) and V of the next chunk as token rows, consumers fold each chunk into
@@ -1375,7 +1348,7 @@ hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
     if constexpr (C == kPcC)
         prefill_pc_kernel<GATED, FM><<<dim3(blocks), dim3(kPcThreads), 0, stream>>>(a);
     else
-        chunk_kernel<C, GATED, FM><<<dim3(blocks), dim3(kThreads), 0, stream>>>(a);
+        prefill_p8_kernel<GATED, FM><<<dim3(blocks), dim3(kP8Threads), 0, stream>>>(a);
     return hipGetLastError();
 }
 
