@@ -82,6 +82,7 @@ CAUSAL = [
     (1, 1, 700, 128, 128, "bf16", 64, False, False),   # several segments
     (2, 2, 77, 16, 24, "f32", 16, True, True),
     (1, 2, 50, 8, 8, "f64", 7, False, True),
+    (1, 1, 1500, 128, 128, "bf16", 128, False, True),  # several segments at chunk 128
 ]
 
 
@@ -103,16 +104,17 @@ def test_causal_prefill_feature_maps(torch, phi, case):
     _compare(Y, S, z, ref, dt, "causal %s %s" % (phi, case))
 
 
-def test_elu1_fm_matches_plain_call_bitwise(torch):
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_elu1_fm_matches_plain_call_bitwise(torch, chunk):
     Q, K, V, alpha, S0, z0 = _inputs(torch, 1, 2, 300, 128, 128, torch.bfloat16, 7, gated=True, with_state=True)
     outs = []
     for fm in (False, True):
         S, z = _state(torch, 1, 2, 128, 128, torch.float32, S0, z0)
         Y = torch.empty_like(V)
         if fm:
-            la.la_prefill_chunked_fm(Q, K, V, alpha, 1e-6, 64, Y, S, z, phi="elu1")
+            la.la_prefill_chunked_fm(Q, K, V, alpha, 1e-6, chunk, Y, S, z, phi="elu1")
         else:
-            la.la_prefill_chunked(Q, K, V, alpha, 1e-6, 64, Y, S, z)
+            la.la_prefill_chunked(Q, K, V, alpha, 1e-6, chunk, Y, S, z)
         torch.cuda.synchronize()
         outs.append((Y.clone(), S.clone(), z.clone()))
     for a, b in zip(*outs):
