@@ -92,6 +92,13 @@ CASES = [
     # more segments than the scan reads in one batch
     (1, 1, 4000, 64, True, True),
     (1, 1, 5000, 128, False, True),
+    # chunk 128 at its edges: one token, one chunk short of full and exactly full, and
+    # several segments of whole and of ragged chunks
+    (1, 2, 1, 128, True, True),
+    (1, 2, 127, 128, True, False),
+    (1, 2, 128, 128, False, True),
+    (1, 2, 2048, 128, False, True),
+    (1, 2, 2049, 128, True, True),
 ]
 
 
