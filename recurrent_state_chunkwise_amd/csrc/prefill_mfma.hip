@@ -668,9 +668,9 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
             for (int tf = 0; tf < 8; ++tf) {
                 const bf16x8 ka = cat8(ld_tr(&Wb[pr_off(tb, tf * 16 + tc)]), ld_tr(&Wb[pr_off(tb + 1, tf * 16 + tc)]));
                 sacc[tf] = mfma(ka, vb, sacc[tf]);
+                if (tf == wave)  // this wave's features of z: the tile just loaded
+                    zr = mfma(ka, ones, zr);
             }
-            const bf16x8 kz = cat8(ld_tr(&Wb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Wb[pr_off(tb + 1, wave * 16 + tc)]));
-            zr = mfma(kz, ones, zr);
         }
         if (lr == 0)
             *reinterpret_cast<f32x4 *>(&sm.zs[buf ^ 1][fw]) = zr;
@@ -1056,9 +1056,14 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
             for (int tf = 0; tf < 8; ++tf) {
                 const bf16x8 ka = cat8(ld_tr(&sm.Kw[pr_off(tb, tf * 16 + tc)]), ld_tr(&sm.Kw[pr_off(tb + 1, tf * 16 + tc)]));
                 sacc[tf] = mfma(ka, vb, sacc[tf]);
+                if (!GATED && tf == wave)  // this wave's features of z: the tile just loaded
+                    zr = mfma(ka, ones, zr);
             }
-            const bf16x8 kz = cat8(ld_tr(&sm.Kw[pr_off(tb, wave * 16 + tc)]), ld_tr(&sm.Kw[pr_off(tb + 1, wave * 16 + tc)]));
-            zr = mfma(kz, ones, zr);
+            if constexpr (GATED) {
+                // the gated instance measured faster with its own load of the z operand
+                const bf16x8 kz = cat8(ld_tr(&sm.Kw[pr_off(tb, wave * 16 + tc)]), ld_tr(&sm.Kw[pr_off(tb + 1, wave * 16 + tc)]));
+                zr = mfma(kz, ones, zr);
+            }
         }
         if (lr == 0)
             *reinterpret_cast<f32x4 *>(&sm.zs[buf ^ 1][fw]) = zr;
