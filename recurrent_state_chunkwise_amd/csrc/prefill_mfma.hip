@@ -114,10 +114,6 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, int off)
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// low / high bf16 halves of two dwords packed into one dword (x in the low half)
-__device__ __forceinline__ unsigned pack_lo(unsigned x, unsigned y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
-__device__ __forceinline__ unsigned pack_hi(unsigned x, unsigned y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
-
 // Gate weights inside a chunk, from lg (the in-chunk prefix sums of log alpha, zero gates
 // left out) and zp (the position of the last zero gate at or before each token, -1 if
 // none).  The weight of token i's write as token j reads it (i <= j) is the product of
