@@ -615,7 +615,14 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         wg_barrier();  // a | b
 
         // ---- part b: (3) with V^T in the score tiles' k order (tokens sigma(4lg4 + e)
-        //      and 16 + sigma(4lg4 + e) of the 32-token step), outputs, then (4)
+        //      and 16 + sigma(4lg4 + e) of the 32-token step), outputs, then (4).  The V^T
+        //      operand of each 32-token step is loaded once and serves every token tile.
+        bf16x8 vt[G::NKI];
+#pragma unroll
+        for (int ki = 0; ki < G::NKI; ++ki) {
+            const int tb = ki * 32 + sigma(lg4 * 4 + te);
+            vt[ki] = cat8(ld_tr(&Vb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Vb[pr_off(tb + 16, wave * 16 + tc)]));
+        }
 #pragma unroll
         for (int tj = 0; tj < G::NTJ; ++tj) {
             const int j = tj * 16 + lr;
@@ -631,9 +638,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
 #pragma unroll
             for (int ki = 0; 2 * ki <= tj; ++ki) {
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, sm.P[(kPairBase[tj] + ki) * 64 + lane]);
-                const int tb = ki * 32 + sigma(lg4 * 4 + te);
-                const bf16x8 va = cat8(ld_tr(&Vb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Vb[pr_off(tb + 16, wave * 16 + tc)]));
-                acc[tj] = mfma(va, pb, acc[tj]);
+                acc[tj] = mfma(vt[ki], pb, acc[tj]);
                 dac = mfma(ones, pb, dac);
             }
             const float inv = __builtin_amdgcn_rcpf(dac[0] + a.eps);
