@@ -111,11 +111,19 @@ def test_mfma_prefill_parity(torch, case):
     _check(Y, S, z, oracle_prefill(Q, K, V, alpha, 1e-6, S0, z0), str(case))
 
 
-@pytest.mark.parametrize("chunk", [64, 128])
-def test_mfma_zero_gates_reset(torch, chunk):
-    Q, K, V, alpha, S0, z0 = _inputs(torch, 1, 2, 300, True, True, 99, zero_gates=True)
+@pytest.mark.parametrize("chunk,T", [(64, 300), (128, 300), (64, 2100), (128, 2100)])
+def test_mfma_zero_gates_reset(torch, chunk, T):
+    """Zero gates wipe the state.  At T=2100 the sequence runs in several segments: zero gates
+    fall inside segments and on the first token of a segment (640 at chunk 64, where segments
+    are 320 tokens; 768 at chunk 128, where they are 384), so segment maps with G = 0 pass
+    through the segment scan."""
+    Q, K, V, alpha, S0, z0 = _inputs(torch, 1, 2, T, True, True, 99 if T == 300 else 99 + T + chunk,
+                                     zero_gates=True)
+    if T > 1000:
+        alpha[..., 640] = 0.0
+        alpha[..., 768] = 0.0
     Y, S, z = _run(torch, Q, K, V, alpha, chunk, S0, z0)
-    _check(Y, S, z, oracle_prefill(Q, K, V, alpha, 1e-6, S0, z0), "zero gates chunk=%d" % chunk)
+    _check(Y, S, z, oracle_prefill(Q, K, V, alpha, 1e-6, S0, z0), "zero gates chunk=%d T=%d" % (chunk, T))
 
 
 @pytest.mark.parametrize("chunk,T", [(64, 300), (128, 300), (64, 2000), (128, 2100)])
