@@ -984,13 +984,6 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
                 dac[0] *= g;
             }
         };
-        auto out_step = [&](int tj, int ki, uint2 p0, uint2 p1, f32x4 &dac) {
-            const bf16x8 pb = cat8(__builtin_bit_cast(bf16x4, p0), __builtin_bit_cast(bf16x4, p1));
-            const int tb = ki * 32 + sigma(lg4 * 4 + te);
-            const bf16x8 va = cat8(ld_tr(&sm.Vs[pr_off(tb, wave * 16 + tc)]), ld_tr(&sm.Vs[pr_off(tb + 16, wave * 16 + tc)]));
-            acc[tj] = mfma(va, pb, acc[tj]);
-            dac = mfma(ones, pb, dac);
-        };
         auto out_end = [&](int tj, const f32x4 &dac) {
             const int j = tj * 16 + lr;
             const float inv = __builtin_amdgcn_rcpf(dac[0] + a.eps);
@@ -1002,39 +995,44 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, yb),
                                                   rY, ((c * C + j) * kD + fw) * 2, 0, 0);
         };
-        if constexpr (GATED) {
-            // token tiles in pairs (2m, 2m + 1): tile 2m has m full pairs of score tiles and
-            // the diagonal tile alone, tile 2m + 1 has m + 1 full pairs, so no score read is
-            // conditional (in the ungated instance this form spills LDS addresses inside the
-            // chunk loop and measured slower than the form below)
+        auto pair = [&](int k0, int k1) {
+            return cat8(__builtin_bit_cast(bf16x4, sm.P[k0 * 64 + lane]), __builtin_bit_cast(bf16x4, sm.P[k1 * 64 + lane]));
+        };
+        // token tiles in pairs (2m, 2m + 1), both fed from each 32-token step's V^T operand:
+        // tile 2m + 1 has m + 1 full pairs of score tiles, tile 2m has m full pairs and the
+        // diagonal tile alone, taken in the last step
 #pragma unroll 1
-            for (int m = 0; m < G::NTJ / 2; ++m) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int tj = 2 * m + h;
-                    const int kbase = tj * (tj + 1) / 2;
-                    f32x4 dac;
-                    out_begin(tj, dac);
-                    for (int ki = 0; ki < m + h; ++ki)
-                        out_step(tj, ki, sm.P[(kbase + 2 * ki) * 64 + lane], sm.P[(kbase + 2 * ki + 1) * 64 + lane], dac);
-                    if (h == 0)
-                        out_step(tj, m, sm.P[(kbase + 2 * m) * 64 + lane], make_uint2(0u, 0u), dac);
-                    out_end(tj, dac);
-                }
+        for (int m = 0; m < G::NTJ / 2; ++m) {
+            const int t0 = 2 * m, t1 = 2 * m + 1;
+            const int kb0 = t0 * (t0 + 1) / 2, kb1 = t1 * (t1 + 1) / 2;
+            f32x4 dac0, dac1;
+            out_begin(t0, dac0);
+            out_begin(t1, dac1);
+            auto vstep = [&](int ki) {
+                const int tb = ki * 32 + sigma(lg4 * 4 + te);
+                return cat8(ld_tr(&sm.Vs[pr_off(tb, wave * 16 + tc)]), ld_tr(&sm.Vs[pr_off(tb + 16, wave * 16 + tc)]));
+            };
+            for (int ki = 0; ki < m; ++ki) {
+                const bf16x8 va = vstep(ki);
+                const bf16x8 pb0 = pair(kb0 + 2 * ki, kb0 + 2 * ki + 1);
+                const bf16x8 pb1 = pair(kb1 + 2 * ki, kb1 + 2 * ki + 1);
+                acc[t0] = mfma(va, pb0, acc[t0]);
+                dac0 = mfma(ones, pb0, dac0);
+                acc[t1] = mfma(va, pb1, acc[t1]);
+                dac1 = mfma(ones, pb1, dac1);
             }
-        } else {
-#pragma unroll 2
-            for (int tj = 0; tj < G::NTJ; ++tj) {
-                const int kbase = tj * (tj + 1) / 2;
-                f32x4 dac;
-                out_begin(tj, dac);
-                for (int ki = 0; 2 * ki <= tj; ++ki) {
-                    const uint2 p0 = sm.P[(kbase + 2 * ki) * 64 + lane];
-                    const uint2 p1 = 2 * ki + 1 <= tj ? sm.P[(kbase + 2 * ki + 1) * 64 + lane] : make_uint2(0u, 0u);
-                    out_step(tj, ki, p0, p1, dac);
-                }
-                out_end(tj, dac);
+            {
+                const bf16x8 va = vstep(m);
+                const bf16x8 pb0 = cat8(__builtin_bit_cast(bf16x4, sm.P[(kb0 + 2 * m) * 64 + lane]),
+                                        __builtin_bit_cast(bf16x4, make_uint2(0u, 0u)));
+                const bf16x8 pb1 = pair(kb1 + 2 * m, kb1 + 2 * m + 1);
+                acc[t0] = mfma(va, pb0, acc[t0]);
+                dac0 = mfma(ones, pb0, dac0);
+                acc[t1] = mfma(va, pb1, acc[t1]);
+                dac1 = mfma(ones, pb1, dac1);
             }
+            out_end(t0, dac0);
+            out_end(t1, dac1);
         }
         const float g_end = GATED ? sm.gj[buf][n - 1] : 1.f;
         if (GATED) {
