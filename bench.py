@@ -88,15 +88,43 @@ def prefill_useful_flops(B, H, T, C, d=128, dv=128):
     return B * H * T * ((C + 1) * (d + dv) + 4 * d * dv)
 
 
+# The clock under load: kernel times change over the first tens of milliseconds of
+# back-to-back work, so every timing warms up for at least WARMUP_FLOOR_S of calls and
+# every mean per call is taken over at least TIMED_FLOOR_S, whatever --warmup and
+# --steps ask for (the timed steps behind `value` are still exactly --steps).
+WARMUP_FLOOR_S = 0.040
+TIMED_FLOOR_S = 0.025
+
+
+def run_for(torch, fn, at_least_calls, floor_s):
+    """Call fn(0), fn(1), ... back to back: at least `at_least_calls` calls and at least
+    `floor_s` seconds of wall time, the device drained before each reading of the clock.
+    Returns (calls, seconds)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n, batch = 0, max(int(at_least_calls), 1)
+    while True:
+        for i in range(batch):
+            fn(n + i)
+        n += batch
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if n >= at_least_calls and el >= floor_s:
+            return n, el
+        batch = max(1, int((floor_s - el) / (el / n) * 1.1) + 1)
+
+
 def time_prefill(torch, la, wl, cfg, steps, warmup, sets=2, noncausal=False):
     """Time la_prefill_chunked (or la_prefill_noncausal); step i uses input set i % sets.
     Two sets of the ungated workload (2 x 201 MB of Q, K, V) exceed the 256 MB last-level
-    cache, so a timed call cannot find its inputs left in it by the previous call.
+    cache, so a timed call cannot find its inputs left there by the previous call.
 
-    Returns (total_ms, call_ms, wall):
-      total_ms  `steps` steps of state initialisation + call, events only around the loop;
-      call_ms   mean time of one call, from `steps` back-to-back calls bracketed by events
-                (the state buffers carry over from call to call: the work is identical).
+    Returns a dict:
+      total_ms  exactly `steps` steps of state initialisation + call, events only around
+                the loop (after a warm-up of at least `warmup` steps and WARMUP_FLOOR_S);
+      call_ms   mean time of one call over `call_calls` back-to-back calls (at least
+                `steps` and at least TIMED_FLOOR_S) bracketed by events; the state buffers
+                carry over from call to call, which leaves the work identical.
     Events are kept out of the loops: each recorded timing event costs several microseconds
     of device time between the kernels it separates."""
     inputs = [wl.prefill_inputs(cfg, "cuda", seed=cfg.seed + 1000 * i) for i in range(sets)]
@@ -111,31 +139,32 @@ def time_prefill(torch, la, wl, cfg, steps, warmup, sets=2, noncausal=False):
         else:
             la.la_prefill_chunked(Q, K, V, A, cfg.eps, cfg.chunk, Y, S, z)
 
-    for i in range(warmup):
+    def step(i):
         la.la_state_init(S, z)
         call(i)
-    torch.cuda.synchronize()
+
+    w_calls, w_s = run_for(torch, step, warmup, WARMUP_FLOOR_S)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
     t_start.record()
     for i in range(steps):
-        la.la_state_init(S, z)
-        call(i)
+        step(i)
     t_end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
+    # the warm-up steps include the state initialisation: 1.5x margin over the call count
+    n_calls = max(steps, int(1.5 * TIMED_FLOOR_S / (w_s / w_calls)) + 1)
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
     c0.record()
-    for i in range(steps):
+    for i in range(n_calls):
         call(i)
     c1.record()
     torch.cuda.synchronize()
-    call_ms = c0.elapsed_time(c1) / steps
+    region_ms = c0.elapsed_time(c1)
     del inputs, Y, S, z
-    return total_ms, call_ms, wall
+    return {"total_ms": total_ms, "call_ms": region_ms / n_calls, "warmup_steps_run": w_calls,
+            "warmup_ms": w_s * 1e3, "call_calls": n_calls, "call_region_ms": region_ms}
 
 
 def time_decode(torch, la, wl, cfg, warmup=10, steps=None):
@@ -153,9 +182,12 @@ def time_decode(torch, la, wl, cfg, warmup=10, steps=None):
     inputs = [wl.decode_step_inputs(cfg, i, "cuda") for i in range(max(steps, warmup))]
     y = torch.empty((N, cfg.dv), device="cuda", dtype=torch.bfloat16)
     Sw, zw = S.clone(), z.clone()
-    for i in range(warmup):  # on a scratch copy of the state
-        q, k, v = inputs[i]
+
+    def warm(i):  # on a scratch copy of the state
+        q, k, v = inputs[i % len(inputs)]
         la.la_decode_step(q, k, v, None, cfg.eps, y, Sw, zw)
+
+    run_for(torch, warm, warmup, WARMUP_FLOOR_S)
     del Sw, zw
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
@@ -182,9 +214,14 @@ def time_delta(torch, la, wl, cfg, warmup=10, steps=None):
     steps = cfg.steps if steps is None else steps
     inputs = [wl.delta_step_inputs(cfg, i, "cuda") for i in range(max(steps, warmup))]
     y = torch.empty((N, cfg.dv), device="cuda", dtype=torch.bfloat16)
-    for i in range(warmup):
-        q, k, v, b = inputs[i]
-        la.la_delta_decode_step(q, k, v, b, y, S)
+    Sw = S.clone()
+
+    def warm(i):  # on a scratch copy of the memories
+        q, k, v, b = inputs[i % len(inputs)]
+        la.la_delta_decode_step(q, k, v, b, y, Sw)
+
+    run_for(torch, warm, warmup, WARMUP_FLOOR_S)
+    del Sw
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -430,22 +467,23 @@ def main():
         return
     if args.only in ("gated", "long"):
         ocfg = wl.PREFILL_GATED if args.only == "gated" else wl.PREFILL_LONG
-        o_total, o_call, _ = time_prefill(torch, la, wl, ocfg, args.steps, args.warmup)
+        r = time_prefill(torch, la, wl, ocfg, args.steps, args.warmup)
         print(json.dumps({"only": args.only, "workload": ocfg.name, "steps": args.steps,
-                          "ms_per_step": o_total / args.steps, "call_ms": o_call}))
+                          "ms_per_step": r["total_ms"] / args.steps, **r}))
         return
     cfg = wl.PREFILL_UNGATED
     if args.only == "noncausal":
-        n_total, n_call, _ = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, noncausal=True)
-        print(json.dumps({"only": "noncausal", "steps": args.steps, "ms_per_step": n_total / args.steps,
-                          "call_ms": n_call}))
+        r = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, noncausal=True)
+        print(json.dumps({"only": "noncausal", "steps": args.steps, "ms_per_step": r["total_ms"] / args.steps,
+                          **r}))
         return
     torch.cuda.synchronize()
-    total_ms, call_ms, wall = time_prefill(torch, la, wl, cfg, args.steps, args.warmup)
+    main_t = time_prefill(torch, la, wl, cfg, args.steps, args.warmup)
+    total_ms, call_ms = main_t["total_ms"], main_t["call_ms"]
     # the same call on one input set, whose inputs may stay in the last-level cache (reported only)
     warm_call_ms = None
     if args.only is None:
-        _, warm_call_ms, _ = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, sets=1)
+        warm_call_ms = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, sets=1)["call_ms"]
     ms_per_step = total_ms / args.steps
     tokens = cfg.B * cfg.T
     value = tokens * args.steps / (total_ms / 1e3)
@@ -459,6 +497,12 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "timing": {"warmup_steps_run": main_t["warmup_steps_run"], "warmup_ms": main_t["warmup_ms"],
+                   "timed_steps": args.steps, "timed_ms": total_ms,
+                   "call_ms_calls": main_t["call_calls"], "call_ms_region_ms": main_t["call_region_ms"],
+                   "floors": "warm-up until >= %d ms of back-to-back steps (and >= --warmup steps); call_ms "
+                             "over >= %d ms of back-to-back calls (and >= --steps calls)"
+                             % (WARMUP_FLOOR_S * 1e3, TIMED_FLOOR_S * 1e3)},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -513,7 +557,7 @@ def main():
                          "traffic": measured_traffic("delta"),
                          "call_ms": x_call, "algorithmic_bytes": x_bytes},
         }
-        n_total, n_call, _ = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, noncausal=True)
+        n_call = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, noncausal=True)["call_ms"]
         out["noncausal"] = {
             "workload": "noncausal_" + cfg.name, "value": tokens / (n_call / 1e3), "unit": "tokens/s",
             "roofline": {"kernel": "la_prefill_noncausal (segment sums + read-out)", "bound": "hbm",
@@ -526,9 +570,7 @@ def main():
         out["kv_vs_state_batched"] = time_kv_state(torch, la, wl, wl.KV_STATE_BATCHED)
         other = []
         for ocfg in (wl.PREFILL_GATED, wl.PREFILL_LONG):
-            # about 30 ms of warm-up: the clock settles only after some tens of ms of load
-            steps, warm = (150, 150) if ocfg.T <= 16384 else (16, 16)
-            o_total, o_call, _ = time_prefill(torch, la, wl, ocfg, steps, warm)
+            o_call = time_prefill(torch, la, wl, ocfg, args.steps, args.warmup)["call_ms"]
             ob = prefill_bytes(ocfg.B, ocfg.H, ocfg.T, ocfg.gated)
             of = prefill_useful_flops(ocfg.B, ocfg.H, ocfg.T, ocfg.chunk)
             other.append({"workload": ocfg.name, "value": ocfg.B * ocfg.T / (o_call / 1e3), "unit": "tokens/s",
