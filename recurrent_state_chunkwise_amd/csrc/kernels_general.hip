@@ -326,9 +326,59 @@ __global__ __launch_bounds__(kThreads) void prefill_general_kernel(
         const int f = e / nc, c = e - f * nc;
         Sh[(int64_t)f * dv + c0 + c] = Ss[f * slice + c];
     }
-    if (blockIdx.y == 0)
-        for (int f = tid; f < d; f += kThreads)
-            zh[f] = zs[f];
+    // z is left to z_finish_kernel: other slices of this sequence may still be about to
+    // read the incoming z
+}
+
+// The final z of each sequence, z_out = (product of all gates) z_in + sum over i of
+// (product of the gates after i) phi(k_i), as the plain recurrence z = alpha z + phi(k)
+// (page "Linear attention：把历史写进状态", sections "每来一个 token" and "加一个门")
+// walked over kZStripes stretches of the sequence at once and composed in order.  It runs
+// after the kernel whose value slices all read the incoming z, so it is the only writer
+// of z.  One workgroup per sequence; thread (p, f) walks stretch p for feature f.
+constexpr int kZThreads = 1024;
+
+template <typename TI, typename TA, int FM>
+__global__ __launch_bounds__(kZThreads) void z_finish_kernel(const TI *__restrict__ K, const TA *__restrict__ alpha,
+                                                             int64_t T, int d, TA *__restrict__ z)
+{
+    __shared__ TA zl[kZThreads];
+    __shared__ TA gp[kZThreads];
+    const int tid = threadIdx.x;
+    const int64_t h = blockIdx.x;
+    const int stripes = kZThreads / d;  // d <= 128: at least 8 stretches
+    const int p = tid / d, f = tid - p * d;
+    const int64_t len = (T + stripes - 1) / stripes;
+    if (p < stripes) {
+        const int64_t t0 = p * len, t1 = min(T, t0 + len);
+        const TI *Kh = K + h * T * d;
+        const TA *Ah = alpha ? alpha + h * T : nullptr;
+        TA acc = TA(0), g = TA(1);
+#pragma unroll 8
+        for (int64_t t = t0; t < t1; ++t) {
+            const TA kf = phi_accurate<FM>(to_acc<TA>(Kh[t * d + f]));
+            const TA a = Ah ? Ah[t] : TA(1);
+            acc = a * acc + kf;
+            g *= a;
+        }
+        zl[tid] = acc;
+        gp[tid] = g;
+    }
+    __syncthreads();
+    if (tid < d) {
+        TA run = z[h * d + tid];
+        for (int q = 0; q < stripes; ++q)
+            run = gp[q * d + tid] * run + zl[q * d + tid];
+        z[h * d + tid] = run;
+    }
+}
+
+template <typename TI, typename TA, int FM>
+hipError_t launch_z_finish(const PrefillArgs &a, hipStream_t stream)
+{
+    z_finish_kernel<TI, TA, FM><<<dim3((unsigned)a.n_heads), dim3(kZThreads), 0, stream>>>(
+        static_cast<const TI *>(a.K), static_cast<const TA *>(a.alpha), a.T, a.d, static_cast<TA *>(a.z));
+    return hipGetLastError();
 }
 
 template <typename TI, typename TA, int FM>
@@ -344,7 +394,10 @@ hipError_t launch_general_typed(const PrefillArgs &a, hipStream_t stream)
         static_cast<const TI *>(a.Q), static_cast<const TI *>(a.K), static_cast<const TI *>(a.V),
         static_cast<const TA *>(a.alpha), a.T, a.d, a.dv, slice, static_cast<TA>(a.eps), a.chunk,
         static_cast<TI *>(a.Y), static_cast<TA *>(a.S), static_cast<TA *>(a.z));
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    return launch_z_finish<TI, TA, FM>(a, stream);
 }
 
 // ===================================================================== general non-causal form
@@ -358,7 +411,8 @@ size_t noncausal_general_lds_bytes(int d, int slice)
 // One workgroup per (sequence, slice of value columns).  First the whole sequence is
 // written into the workgroup's slice of the state (and into all of z, which every
 // slice needs), kIB tokens at a time; the state goes back to the caller; then every
-// query is read against it, kRB rows at a time.  Slice 0 writes z.
+// query is read against it, kRB rows at a time.  No slice writes z: z_finish_kernel
+// does, once every slice has read the incoming z.
 template <typename TI, typename TA, int FM>
 __global__ __launch_bounds__(kThreads) void noncausal_general_kernel(
     const TI *__restrict__ Q, const TI *__restrict__ K, const TI *__restrict__ V, int64_t T, int d, int dv,
@@ -436,11 +490,8 @@ __global__ __launch_bounds__(kThreads) void noncausal_general_kernel(
             Sh[(int64_t)f * dv + c0 + c] = sreg[p];
         }
     }
-    if (tid < d) {
-        zs[tid] = zreg;
-        if (blockIdx.y == 0)
-            zh[tid] = zreg;
-    }
+    if (tid < d)
+        zs[tid] = zreg;  // z goes out through z_finish_kernel, after every slice has read z_in
 
     // ---------------- read: every query against the full state
     for (int64_t j0 = 0; j0 < T; j0 += kRB) {
@@ -490,7 +541,10 @@ hipError_t launch_noncausal_typed(const PrefillArgs &a, hipStream_t stream)
     noncausal_general_kernel<TI, TA, FM><<<dim3((unsigned)a.n_heads, n_slices), dim3(kThreads), lds, stream>>>(
         static_cast<const TI *>(a.Q), static_cast<const TI *>(a.K), static_cast<const TI *>(a.V), a.T, a.d, a.dv,
         slice, static_cast<TA>(a.eps), static_cast<TI *>(a.Y), static_cast<TA *>(a.S), static_cast<TA *>(a.z));
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    return launch_z_finish<TI, TA, FM>(a, stream);  // PrefillArgs of the non-causal form carry no alpha
 }
 
 // ===================================================================== decode

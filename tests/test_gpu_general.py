@@ -129,6 +129,27 @@ def test_general_prefill_parity(torch, case, io):
         assert_prefill_parity(Y, S, z, ref, bar, str(case))
 
 
+@pytest.mark.parametrize("form,gated", [("causal", False), ("causal", True), ("noncausal", False)])
+def test_general_many_sequences_nonzero_state(torch, form, gated):
+    """f32, d = dv = 128, 2,048 sequences with a nonzero incoming S and z: 8,192 workgroups
+    (sequence x value slice), more than the GPU holds at once, so the slices of one sequence
+    start at different times.  Every slice must read the caller's z, and the final z must
+    be written only after all of them have read it."""
+    from helpers import oracle_noncausal
+    B, H, T, d, dv = 16, 128, 24, 128, 128
+    Q, K, V, alpha, S0, z0 = _case_inputs(torch, B, H, T, d, dv, gated, True, torch.float32, 4242)
+    if form == "causal":
+        Y, S, z = _run_prefill(torch, Q, K, V, alpha, 1e-6, 16, S0, z0)
+        ref = oracle_prefill(Q, K, V, alpha, 1e-6, S0, z0)
+    else:
+        Y, S, z = torch.empty_like(V), S0.clone(), z0.clone()
+        la.la_prefill_noncausal(Q, K, V, 1e-6, Y, S, z)
+        torch.cuda.synchronize()
+        ref = oracle_noncausal(Q, K, V, 1e-6, S0, z0)
+    m = assert_prefill_parity(Y, S, z, ref, "f32", "%s gated=%s" % (form, gated))
+    print("many sequences", form, gated, m)
+
+
 def test_general_prefill_causality_bitwise(torch):
     """Changing later tokens leaves earlier outputs bit-identical."""
     Q, K, V, alpha, S0, z0 = _case_inputs(torch, 1, 2, 90, 32, 16, True, True, torch.float32, 77)
