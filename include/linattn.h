@@ -21,6 +21,8 @@
  *     arrays owned by the caller.  The library allocates nothing, keeps nothing
  *     between calls and never synchronises: work is enqueued on `stream`
  *     (a hipStream_t; NULL means the default stream) and the caller synchronises.
+ *     (One exception: la_softmax_decode_step_static keeps its scratch in a fixed
+ *     device array of the library's own, see there.)
  *   - Arguments are checked on the host before anything is enqueued.  On any
  *     status other than LA_OK nothing has been launched and no output has been
  *     written.  Faults inside a kernel surface at the caller's next
@@ -53,7 +55,7 @@ typedef enum la_status {
     LA_ERR_EPS = 4,         /* eps is negative, NaN or infinite (0 is allowed) */
     LA_ERR_CHUNK = 5,       /* chunk < 1 */
     LA_ERR_UNSUPPORTED = 6, /* valid request with no kernel: d or dv > 128, chunk > 128 */
-    LA_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
+    LA_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch (or a set-up call) */
     LA_ERR_ALIAS = 8,       /* an output overlaps an input or another output */
     LA_ERR_PHI = 9,         /* unknown feature map */
     LA_ERR_WORKSPACE = 10,  /* workspace missing or too small */
@@ -246,6 +248,31 @@ la_status la_softmax_decode_step(const void *q, const void *k, const void *v, la
 /* Workspace bytes la_softmax_decode_step needs for a history of L rows (L = pos + 1);
  * 0 when none is needed, -1 for invalid arguments. */
 int64_t la_softmax_decode_workspace_bytes(la_dtype io_dtype, int64_t n_heads, int64_t L, int32_t dv);
+
+/*
+ * la_softmax_decode_step_static -- la_softmax_decode_step with no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It runs the same kernels on the same arguments
+ * (minus workspace and workspace_bytes) and gives bitwise the same y and caches.
+ *   Scratch: the per-piece partials live in a device array of the library's own,
+ *   LA_SOFTMAX_STATIC_WORKSPACE_BYTES bytes on each GPU the call runs on, set up on the
+ *   first call on that device (with it current) and held until the process ends.  The
+ *   call allocates nothing (no hipMalloc, hipFree or allocating library routine).  Every
+ *   entry of the array that a call reads was written earlier in the same call, so
+ *   nothing needs clearing between calls.
+ *   Concurrency: every call on one GPU shares that GPU's array.  Calls whose execution
+ *   overlaps on one GPU (different streams without ordering between them) race and may
+ *   return wrong results; serialise them (one stream, or events).
+ * Errors: those of la_softmax_decode_step, with LA_ERR_WORKSPACE when
+ * la_softmax_decode_workspace_bytes(io_dtype, n_heads, pos + 1, dv) exceeds
+ * LA_SOFTMAX_STATIC_WORKSPACE_BYTES (nothing launched), and LA_ERR_LAUNCH when the runtime
+ * does not give the array's device address on the first call on a device.
+ */
+#define LA_SOFTMAX_STATIC_WORKSPACE_BYTES ((int64_t)32 << 20)
+la_status la_softmax_decode_step_static(const void *q, const void *k, const void *v, la_dtype io_dtype,
+                                        int64_t n_heads, int32_t d, int32_t dv, int64_t pos,
+                                        int64_t capacity, void *K_cache, void *V_cache, double scale,
+                                        void *y, hipStream_t stream);
 
 /* Static description of a status code; never NULL. */
 const char *la_status_str(la_status status);

@@ -23,6 +23,7 @@ __all__ = [
     "FEATURE_MAPS", "LaArgumentError", "LaLaunchError",
     "la_state_init", "la_prefill_chunked", "la_prefill_chunked_fm", "la_prefill_noncausal", "la_decode_step",
     "la_decode_step_fm", "la_delta_decode_step", "la_softmax_decode_step", "la_softmax_decode_workspace_bytes",
+    "la_softmax_decode_step_static", "LA_SOFTMAX_STATIC_WORKSPACE_BYTES",
     "la_status_str", "la_prefill_variant", "library", "library_path",
 ]
 
@@ -38,6 +39,7 @@ STATUS = {
     10: "LA_ERR_WORKSPACE", 11: "LA_ERR_SCALE",
 }
 LA_ERR_LAUNCH = 7
+LA_SOFTMAX_STATIC_WORKSPACE_BYTES = 32 << 20  # the library's fixed scratch per GPU (linattn.h)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblinattn.so")
@@ -101,6 +103,9 @@ def library() -> ctypes.CDLL:
             lib.la_softmax_decode_step.restype = ctypes.c_int
             lib.la_softmax_decode_step.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, i32, i64, i64, vp, vp, f64,
                                                    vp, vp, i64, vp]
+            lib.la_softmax_decode_step_static.restype = ctypes.c_int
+            lib.la_softmax_decode_step_static.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, i32, i64, i64, vp, vp,
+                                                          f64, vp, vp]
             lib.la_softmax_decode_workspace_bytes.restype = i64
             lib.la_softmax_decode_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
             lib.la_prefill_variant.restype = ctypes.c_int32
@@ -331,15 +336,8 @@ def la_softmax_decode_workspace_bytes(io_dtype: int, n_heads: int, L: int, dv: i
     return int(library().la_softmax_decode_workspace_bytes(int(io_dtype), int(n_heads), int(L), int(dv)))
 
 
-def la_softmax_decode_step(q, k, v, pos: int, K_cache, V_cache, y, scale=None, workspace=None,
-                           stream=None) -> None:
-    """Softmax attention decode over an explicit history: row `pos` of the caches takes
-    (k, v), then y = softmax(scale * K_cache[:pos+1] q) V_cache[:pos+1] per head.
-
-    q, k: [H, d]; v, y: [H, dv]; K_cache: [H, capacity, d]; V_cache: [H, capacity, dv];
-    scale defaults to 1/sqrt(d).  A workspace (uint8 device tensor) is allocated here
-    when the call needs one and none is given.
-    """
+def _softmax_shapes(q, k, v, K_cache, V_cache, y):
+    """(H, d, dv, capacity, io) of a softmax decode call, after the shape checks."""
     if q.dim() != 2 or tuple(k.shape) != tuple(q.shape):
         raise ValueError("q and k must both be [H, d] with the same shape")
     H, d = q.shape
@@ -352,7 +350,19 @@ def la_softmax_decode_step(q, k, v, pos: int, K_cache, V_cache, y, scale=None, w
     if tuple(V_cache.shape) != (H, cap, dv):
         raise ValueError("V_cache must be [H, capacity, dv] with K_cache's capacity")
     _same_dtype("q, k, v, y, K_cache, V_cache", (q, k, v, y, K_cache, V_cache))
-    io = _dtype_code(q)
+    return H, d, dv, cap, _dtype_code(q)
+
+
+def la_softmax_decode_step(q, k, v, pos: int, K_cache, V_cache, y, scale=None, workspace=None,
+                           stream=None) -> None:
+    """Softmax attention decode over an explicit history: row `pos` of the caches takes
+    (k, v), then y = softmax(scale * K_cache[:pos+1] q) V_cache[:pos+1] per head.
+
+    q, k: [H, d]; v, y: [H, dv]; K_cache: [H, capacity, d]; V_cache: [H, capacity, dv];
+    scale defaults to 1/sqrt(d).  A workspace (uint8 device tensor) is allocated here
+    when the call needs one and none is given.
+    """
+    H, d, dv, cap, io = _softmax_shapes(q, k, v, K_cache, V_cache, y)
     sc = 1.0 / d ** 0.5 if scale is None else float(scale)
     need = la_softmax_decode_workspace_bytes(io, H, int(pos) + 1, dv) if 0 <= int(pos) < cap else 0
     if need > 0 and workspace is None:
@@ -362,6 +372,18 @@ def la_softmax_decode_step(q, k, v, pos: int, K_cache, V_cache, y, scale=None, w
     rc = library().la_softmax_decode_step(ptrs[0], ptrs[1], ptrs[2], io, H, d, dv, int(pos), cap, ptrs[3], ptrs[4],
                                           sc, ptrs[5], ptrs[6], wbytes, _stream_ptr(q, stream))
     _check(rc, "la_softmax_decode_step")
+
+
+def la_softmax_decode_step_static(q, k, v, pos: int, K_cache, V_cache, y, scale=None, stream=None) -> None:
+    """la_softmax_decode_step without a workspace: the library's fixed per-GPU scratch
+    (LA_SOFTMAX_STATIC_WORKSPACE_BYTES) holds the partials, so the call allocates nothing.
+    Calls that overlap in time on one GPU share that scratch and race."""
+    H, d, dv, cap, io = _softmax_shapes(q, k, v, K_cache, V_cache, y)
+    sc = 1.0 / d ** 0.5 if scale is None else float(scale)
+    ptrs = _device_ptrs(q, k, v, K_cache, V_cache, y)
+    rc = library().la_softmax_decode_step_static(ptrs[0], ptrs[1], ptrs[2], io, H, d, dv, int(pos), cap, ptrs[3],
+                                                 ptrs[4], sc, ptrs[5], _stream_ptr(q, stream))
+    _check(rc, "la_softmax_decode_step_static")
 
 
 def la_prefill_variant(io_dtype: int, d: int, dv: int, chunk: int, gated: bool, state_dtype: int) -> int:

@@ -91,6 +91,45 @@ la_status check_prefill_scalars(la_dtype io, int32_t d, int32_t dv, int32_t chun
     return LA_OK;
 }
 
+// Checks shared by the softmax decode entry points; *need receives the scratch bytes.
+la_status check_softmax(const void *q, const void *k, const void *v, la_dtype io_dtype, int64_t n_heads, int32_t d,
+                        int32_t dv, int64_t pos, int64_t capacity, void *K_cache, void *V_cache, double scale,
+                        void *y, int64_t *need)
+{
+    if (!q || !k || !v || !K_cache || !V_cache || !y)
+        return LA_ERR_NULL;
+    if (n_heads < 1 || d < 1 || dv < 1 || pos < 0 || capacity <= pos || n_heads > INT32_MAX)
+        return LA_ERR_SHAPE;
+    if (!known_dtype(io_dtype))
+        return LA_ERR_DTYPE;
+    if (d > LA_MAX_WIDTH || dv > LA_MAX_WIDTH)
+        return LA_ERR_UNSUPPORTED;
+    if (!isfinite(scale))
+        return LA_ERR_SCALE;
+    int64_t qk, vy, kc, vc;
+    const int64_t ei = dtype_bytes(io_dtype);
+    if (!prod_ok({n_heads, d, ei}, &qk) || !prod_ok({n_heads, dv, ei}, &vy) ||
+        !prod_ok({n_heads, capacity, d, ei}, &kc) || !prod_ok({n_heads, capacity, dv, ei}, &vc) ||
+        la::softmax_decode_splits(pos + 1) > INT32_MAX)
+        return LA_ERR_SHAPE;
+    *need = la_softmax_decode_workspace_bytes(io_dtype, n_heads, pos + 1, dv);
+    if (*need < 0)
+        return LA_ERR_SHAPE;
+    if (any_alias({{K_cache, kc}, {V_cache, vc}, {y, vy}}, {{q, qk}, {k, qk}, {v, vy}}))
+        return LA_ERR_ALIAS;
+    return LA_OK;
+}
+
+// The caller's workspace must not overlap the caches, y or the inputs.
+bool softmax_outputs_alias(const void *q, const void *k, const void *v, la_dtype io_dtype, int64_t n_heads, int32_t d,
+                           int32_t dv, int64_t capacity, void *K_cache, void *V_cache, void *y, Range ws)
+{
+    const int64_t ei = dtype_bytes(io_dtype);
+    const int64_t qk = n_heads * d * ei, vy = n_heads * dv * ei;
+    const int64_t kc = n_heads * capacity * d * ei, vc = n_heads * capacity * dv * ei;
+    return any_alias({ws}, {{q, qk}, {k, qk}, {v, vy}, {K_cache, kc}, {V_cache, vc}, {y, vy}});
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,7 +158,8 @@ const char *la_status_str(la_status s)
     case LA_ERR_PHI:
         return "unknown feature map";
     case LA_ERR_WORKSPACE:
-        return "workspace missing or smaller than la_softmax_decode_workspace_bytes";
+        return "workspace missing or smaller than la_softmax_decode_workspace_bytes (static variant: the call "
+               "needs more than LA_SOFTMAX_STATIC_WORKSPACE_BYTES)";
     case LA_ERR_SCALE:
         return "scale must be finite";
     }
@@ -306,32 +346,36 @@ la_status la_softmax_decode_step(const void *q, const void *k, const void *v, la
                                  int32_t d, int32_t dv, int64_t pos, int64_t capacity, void *K_cache, void *V_cache,
                                  double scale, void *y, void *workspace, int64_t workspace_bytes, hipStream_t stream)
 {
-    if (!q || !k || !v || !K_cache || !V_cache || !y)
-        return LA_ERR_NULL;
-    if (n_heads < 1 || d < 1 || dv < 1 || pos < 0 || capacity <= pos || n_heads > INT32_MAX)
-        return LA_ERR_SHAPE;
-    if (!known_dtype(io_dtype))
-        return LA_ERR_DTYPE;
-    if (d > LA_MAX_WIDTH || dv > LA_MAX_WIDTH)
-        return LA_ERR_UNSUPPORTED;
-    if (!isfinite(scale))
-        return LA_ERR_SCALE;
-    int64_t qk, vy, kc, vc;
-    const int64_t ei = dtype_bytes(io_dtype);
-    if (!prod_ok({n_heads, d, ei}, &qk) || !prod_ok({n_heads, dv, ei}, &vy) ||
-        !prod_ok({n_heads, capacity, d, ei}, &kc) || !prod_ok({n_heads, capacity, dv, ei}, &vc) ||
-        la::softmax_decode_splits(pos + 1) > INT32_MAX)
-        return LA_ERR_SHAPE;
-    const int64_t need = la_softmax_decode_workspace_bytes(io_dtype, n_heads, pos + 1, dv);
-    if (need < 0)
-        return LA_ERR_SHAPE;
+    int64_t need = 0;
+    la_status st = check_softmax(q, k, v, io_dtype, n_heads, d, dv, pos, capacity, K_cache, V_cache, scale, y, &need);
+    if (st != LA_OK)
+        return st;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return LA_ERR_WORKSPACE;
-    if (any_alias({{K_cache, kc}, {V_cache, vc}, {y, vy}, {need > 0 ? workspace : nullptr, need}},
-                  {{q, qk}, {k, qk}, {v, vy}}))
+    if (need > 0 && softmax_outputs_alias(q, k, v, io_dtype, n_heads, d, dv, capacity, K_cache, V_cache, y,
+                                          {workspace, need}))
         return LA_ERR_ALIAS;
 
     la::SoftmaxDecodeArgs a{q, k, v, n_heads, d, dv, pos, capacity, K_cache, V_cache, scale, y, workspace};
+    (void)hipGetLastError();
+    return launched(la::launch_softmax_decode(a, io_dtype, stream));
+}
+
+la_status la_softmax_decode_step_static(const void *q, const void *k, const void *v, la_dtype io_dtype,
+                                        int64_t n_heads, int32_t d, int32_t dv, int64_t pos, int64_t capacity,
+                                        void *K_cache, void *V_cache, double scale, void *y, hipStream_t stream)
+{
+    int64_t need = 0;
+    la_status st = check_softmax(q, k, v, io_dtype, n_heads, d, dv, pos, capacity, K_cache, V_cache, scale, y, &need);
+    if (st != LA_OK)
+        return st;
+    if (need > LA_SOFTMAX_STATIC_WORKSPACE_BYTES)
+        return LA_ERR_WORKSPACE;
+    void *scratch = nullptr;
+    if (need > 0 && la::softmax_static_workspace(&scratch) != hipSuccess)
+        return LA_ERR_LAUNCH;
+
+    la::SoftmaxDecodeArgs a{q, k, v, n_heads, d, dv, pos, capacity, K_cache, V_cache, scale, y, scratch};
     (void)hipGetLastError();
     return launched(la::launch_softmax_decode(a, io_dtype, stream));
 }

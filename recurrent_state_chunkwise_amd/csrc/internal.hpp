@@ -80,6 +80,9 @@ hipError_t launch_delta_decode(const DeltaArgs &a, la_dtype io_dtype, hipStream_
 hipError_t launch_softmax_decode(const SoftmaxDecodeArgs &a, la_dtype io_dtype, hipStream_t stream);
 // history pieces (workgroups per head) of the softmax decode for L attended rows
 int64_t softmax_decode_splits(int64_t L);
+// Device address of the softmax decode's fixed scratch array on the current device
+// (LA_SOFTMAX_STATIC_WORKSPACE_BYTES bytes), looked up once per device.
+hipError_t softmax_static_workspace(void **ptr);
 
 // True when the bf16 MFMA prefill kernel handles the request.
 bool mfma_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk);

@@ -13,6 +13,8 @@
 // second kernel combines the pieces of a head with the usual rescaling by exp(m - M).
 // The workgroup that owns row `pos` takes that row's key and value from the inputs and
 // writes them to the caches; no other workgroup reads it.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -386,7 +388,38 @@ hipError_t launch_softmax_typed(const SoftmaxDecodeArgs &s, hipStream_t stream)
     return hipGetLastError();
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+// The fixed scratch of la_softmax_decode_step_static.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device (each GPU holds its own copy).
+static __device__ __align__(256) unsigned char scratch[LA_SOFTMAX_STATIC_WORKSPACE_BYTES];
+
+hipError_t softmax_static_workspace(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 int64_t softmax_decode_splits(int64_t L) { return (L + kSplit - 1) / kSplit; }
 

@@ -263,3 +263,30 @@ def test_softmax_decode_rejections(lib):
     assert softmax(lib, Kc=ctypes.c_void_p(P[2].value + 8)) == ALIAS
     assert softmax(lib, Vc=P[3]) == ALIAS
     assert softmax(lib, pos=300, cap=512, ws=P[5]) == ALIAS
+
+
+def softmax_static(lib, q=P[0], k=P[1], v=P[2], io=BF16, H=2, d=64, dv=64, pos=10, cap=16, Kc=P[3], Vc=P[4],
+                   scale=0.125, y=P[5]):
+    return lib.la_softmax_decode_step_static(q, k, v, io, H, d, dv, pos, cap, Kc, Vc, scale, y, None)
+
+
+def test_softmax_decode_static_rejections(lib):
+    """The allocation-free variant checks its arguments like la_softmax_decode_step and
+    refuses, before any launch, a call whose partials exceed its fixed scratch."""
+    assert la.LA_SOFTMAX_STATIC_WORKSPACE_BYTES == 32 << 20
+    assert softmax_static(lib, q=None) == NULL
+    assert softmax_static(lib, Vc=None) == NULL
+    assert softmax_static(lib, H=0) == SHAPE
+    assert softmax_static(lib, pos=16, cap=16) == SHAPE
+    assert softmax_static(lib, io=9) == DTYPE
+    assert softmax_static(lib, dv=129) == UNSUP
+    assert softmax_static(lib, scale=math.inf) == SCALE
+    assert softmax_static(lib, y=P[1]) == ALIAS
+    # 4,096 heads over 8,192 rows at dv = 128: 4096 x 32 pieces x 130 floats = 68 MB of
+    # partials, beyond the 32 MiB array (buffers placed 1 TiB apart so none overlap)
+    far = [ctypes.c_void_p((1 << 40) * (i + 1)) for i in range(6)]
+    big = dict(q=far[0], k=far[1], v=far[2], Kc=far[3], Vc=far[4], y=far[5], H=4096, d=128, dv=128,
+               pos=8191, cap=8192)
+    need = la.la_softmax_decode_workspace_bytes(BF16, 4096, 8192, 128)
+    assert need == 4096 * 32 * 130 * 4 > la.LA_SOFTMAX_STATIC_WORKSPACE_BYTES
+    assert softmax_static(lib, **big) == WORKSPACE
