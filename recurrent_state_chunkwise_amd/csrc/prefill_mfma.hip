@@ -220,8 +220,11 @@ __device__ __forceinline__ float *slot_ptr(const Args &a, int64_t head, int p)
 //            producers: y of chunk i-1 to HBM; gate scan of chunk i+1; phi(q) and V of chunk i+1
 //   part b   consumers: gates, V^T P^T and 1^T P^T, y into LDS, state and z update
 //            producers: phi(k) and the write weights of chunk i+1
-// Each raw load is issued two chunks ahead of its use.  The two roles run their own
-// loops with the same number of barriers, which keeps their registers apart.
+// Each raw load is issued two chunks ahead of its use, except K in the gated form, which
+// has one register set and is loaded one chunk ahead: the gated producers also hold the
+// fp32 sums of the z update, and a second K set would not fit in their registers.  The two
+// roles run their own loops with the same number of barriers, which keeps their registers
+// apart.
 //
 // Every staged tile is token-major (one row of 128 bf16 per token, rows padded to
 // 272 bytes), written with 16-byte row stores.  Operands that contract over tokens (V^T
@@ -283,6 +286,21 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi)
 {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
+// z in bf16 high and low parts: hi = bf16(z), lo = bf16(z - hi), so that hi + lo carries
+// about 16 bits of z
+__device__ __forceinline__ void split_store(float z, bf16 *hi, bf16 *lo)
+{
+    const bf16 h = static_cast<bf16>(z);
+    *hi = h;
+    *lo = static_cast<bf16>(z - static_cast<float>(h));
+}
+// A-operands of the denominator product phi(q) . z from the high and low parts zhl[0],
+// zhl[1]: features f0 .. f0 + 3 and f0 + 16 .. f0 + 19 (the k order of the Q~ operand)
+__device__ __forceinline__ void z_operand(const bf16 (&zhl)[2][kD], int f0, bf16x8 &zh, bf16x8 &zl)
+{
+    zh = cat8(*reinterpret_cast<const bf16x4 *>(&zhl[0][f0]), *reinterpret_cast<const bf16x4 *>(&zhl[0][f0 + 16]));
+    zl = cat8(*reinterpret_cast<const bf16x4 *>(&zhl[1][f0]), *reinterpret_cast<const bf16x4 *>(&zhl[1][f0 + 16]));
+}
 
 // score tile (tj, ti) lives in half ti & 1 of pair slot kPairBase[tj] + ti / 2
 constexpr int kPairBase[4] = {0, 1, 2, 4};
@@ -300,6 +318,8 @@ struct alignas(16) PcSmem {
     alignas(16) bf16 Ys[GATED ? 8 : kPcC * kD];
     alignas(16) uint4 P[kPairSlots * 64];          // bf16 score tiles in pairs, 4 values of each per lane
     alignas(16) float zs[2][kD];                   // z entering the chunk, by chunk parity
+    alignas(16) bf16 zhl[2][2][kD];                // the same as bf16 high and low parts
+    alignas(16) float zred[16][kD];                // fp32 z update of the staged chunk, per token group
     alignas(16) float dq[kPcC];                    // phi(q_j) . z_prev
     alignas(16) float lg[2][kPcC];
     alignas(16) float gj[2][kPcC];
@@ -354,6 +374,22 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         // two register sets: chunk c is loaded into set c & 1 two chunks before it is staged
         uint4 rq0[TPT], rk0[TPT], rv0[TPT], rq1[TPT], rk1[TPT], rv1[TPT];
         float ar0 = 0.f, ar1 = 0.f;
+        // z of feature pt (threads pt < 128): z = g_end z + sum of w phi(k) over each chunk,
+        // from the fp32 write weights before their rounding to bf16.  The running value
+        // stays in sm.zs (only this same thread writes and reads it), so it takes no register
+        // across the loop; the consumers read its bf16 high and low parts in sm.zhl.
+        auto z_update = [&](int c) {  // chunk c staged: z entering chunk c + 1, for part a
+            if (pt < kD) {
+                float dz = 0.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    dz += sm.zred[t][pt];
+                const float g = GATED ? sm.gj[c & 1][chunk_len(c) - 1] : 1.f;
+                const float zn = g * sm.zs[c & 1][pt] + dz;
+                sm.zs[(c + 1) & 1][pt] = zn;
+                split_store(zn, &sm.zhl[(c + 1) & 1][0][pt], &sm.zhl[(c + 1) & 1][1][pt]);
+            }
+        };
 
         auto load_qv = [&](int c, uint4 (&rq)[TPT], uint4 (&rv)[TPT]) {
 #pragma unroll
@@ -404,6 +440,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         // ungated weights are phi(k) itself, so those rows of Ks are zeroed instead (the
         // scores never use them: they lie above the diagonal of every kept row).
         auto stage_k = [&](int buf, int gs, int n, const uint4 (&rk)[TPT]) {
+            float zp8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int p = 0; p < TPT; ++p) {
                 const int j = tg * TPT + p;
@@ -417,6 +454,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                     kb[s] = static_cast<bf16>(f);
                     if (GATED)
                         kwb[s] = static_cast<bf16>(w * f);
+                    zp8[s] += GATED ? w * f : (j < n ? f : 0.f);
                 }
                 uint4 u = *reinterpret_cast<uint4 *>(&kb);
                 if (!GATED && j >= n)
@@ -425,6 +463,8 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 if (GATED)
                     *reinterpret_cast<bf16x8 *>(&sm.Kw[buf][pr_off(j, fg * 8)]) = kwb;
             }
+            *reinterpret_cast<f32x4 *>(&sm.zred[tg][fg * 8]) = f32x4{zp8[0], zp8[1], zp8[2], zp8[3]};
+            *reinterpret_cast<f32x4 *>(&sm.zred[tg][fg * 8 + 4]) = f32x4{zp8[4], zp8[5], zp8[6], zp8[7]};
         };
         // y of chunk c from the LDS tile to HBM as whole 256-byte rows: producer wave pw
         // takes rows 4 TPT pw .. 4 TPT pw + 4 TPT - 1, four rows per store; rows past the end
@@ -449,6 +489,8 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         auto step = [&](int i, uint4 (&rq)[TPT], uint4 (&rk)[TPT], uint4 (&rv)[TPT], float &ar) {
             const int cn = i + 1;
             const bool work = cn < n_chunks;
+            if (i < n_chunks)
+                z_update(i);
             flush_y(i > 0 ? i - 1 : n_chunks);
             if (work)
                 scan(chunk_len(cn), cn & 1, ar);
@@ -458,8 +500,11 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
             load_qv(cn + 2, rq, rv);
             wg_barrier();  // a | b
             if (work)
-                stage_k(cn & 1, cn & 1, chunk_len(cn), rk);
-            load_k(cn + 2, rk);
+                stage_k(cn & 1, cn & 1, chunk_len(cn), GATED ? rk0 : rk);
+            if (GATED)
+                load_k(cn + 1, rk0);
+            else
+                load_k(cn + 2, rk);
             wg_barrier();  // chunk i done
         };
 
@@ -468,7 +513,8 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         load_k(0, rk0);
         load_a(0, ar0);
         load_qv(1, rq1, rv1);
-        load_k(1, rk1);
+        if (!GATED)
+            load_k(1, rk1);
         load_a(1, ar1);
         scan(chunk_len(0), 0, ar0);
         load_a(2, ar0);
@@ -476,7 +522,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         stage_qv(0, rq0, rv0);
         load_qv(2, rq0, rv0);
         stage_k(0, 0, chunk_len(0), rk0);
-        load_k(2, rk0);
+        load_k(GATED ? 1 : 2, rk0);
         wg_barrier();
 
         for (int i = 0; i < n_steps; i += 2) {
@@ -486,6 +532,8 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         // the last chunk's y, complete since the last barrier (already written by the
         // trailing empty step when the chunk count is odd)
         flush_y(n_steps == n_chunks ? n_chunks - 1 : n_chunks);
+        if (seg == a.nseg - 1 && pt < kD)
+            a.z[head * kD + pt] = sm.zs[n_chunks & 1][pt];
         return;
     }
 
@@ -494,10 +542,9 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
 #pragma unroll
     for (int s = 0; s < 8; ++s)
         ones[s] = static_cast<bf16>(1.f);
-    // wave w owns value columns c = 16w + lr of S (tile tf holds rows f = 16tf + 4lg4 + r)
-    // and features f = 16w + 4lg4 + r of z
+    // wave w owns value columns c = 16w + lr of S (tile tf holds rows f = 16tf + 4lg4 + r);
+    // z lives with the producers, which pass each chunk's entering z through sm.zhl
     f32x4 sacc[8];
-    f32x4 zr;
     const int cw = wave * 16 + lr;
     const int fw = wave * 16 + lg4 * 4;
     {
@@ -508,11 +555,10 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 sacc[tf][r] = Sin[(tf * 16 + lg4 * 4 + r) * kD + cw];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            zr[r] = zin[fw + r];
-        if (tid < kD)
+        if (tid < kD) {
             sm.zs[0][tid] = zin[tid];
+            split_store(zin[tid], &sm.zhl[0][0][tid], &sm.zhl[0][1][tid]);
+        }
     }
     // transposing-load addresses: this lane supplies 4 adjacent columns (4 (lr & 3) ..)
     // of token row e = lr >> 2 of its group's set
@@ -568,23 +614,20 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 *reinterpret_cast<uint2 *>(&pk);
         }
         // waves 4-7: phi(q_j) . z_prev for the token tile tj = wave - 4, with z_prev
-        // spread over 16 identical columns
+        // spread over 16 identical columns and split into bf16 high and low parts (about
+        // 16 bits of z_prev reach the product)
         if (wave >= 4) {
             const int j = (wave - 4) * 16 + lr;
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kf = 0; kf < 4; ++kf) {
-                const f32x4 zlo = *reinterpret_cast<const f32x4 *>(&sm.zs[buf][kf * 32 + lg4 * 4]);
-                const f32x4 zhi = *reinterpret_cast<const f32x4 *>(&sm.zs[buf][kf * 32 + 16 + lg4 * 4]);
-                bf16x8 zb;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    zb[r] = static_cast<bf16>(zlo[r]);
-                    zb[4 + r] = static_cast<bf16>(zhi[r]);
-                }
+                bf16x8 zh, zl;
+                z_operand(sm.zhl[buf], kf * 32 + lg4 * 4, zh, zl);
                 const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, kf * 32 + lg4 * 4)]);
                 const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&Qb[pr_off(j, opaque(kf * 32 + 16 + lg4 * 4))]);
-                d = mfma(zb, cat8(lo, hi), d);
+                const bf16x8 qv = cat8(lo, hi);
+                d = mfma(zh, qv, d);
+                d = mfma(zl, qv, d);
             }
             if (lg4 == 0)
                 sm.dq[j] = d[0];
@@ -655,9 +698,6 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sacc[tf][r] *= g_end;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                zr[r] *= g_end;
         }
         // (4) in k order: lane group lg4 takes tokens 8lg4 + 2e (first load) and
         //     8lg4 + 2e + 1 (second) of each 32-token step, alike for both operands
@@ -669,29 +709,19 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
             for (int tf = 0; tf < 8; ++tf) {
                 const bf16x8 ka = cat8(ld_tr(&Wb[pr_off(tb, tf * 16 + tc)]), ld_tr(&Wb[pr_off(tb + 1, tf * 16 + tc)]));
                 sacc[tf] = mfma(ka, vb, sacc[tf]);
-                if (tf == wave)  // this wave's features of z: the tile just loaded
-                    zr = mfma(ka, ones, zr);
             }
         }
-        if (lr == 0)
-            *reinterpret_cast<f32x4 *>(&sm.zs[buf ^ 1][fw]) = zr;
         wg_barrier();  // chunk i done
     }
 
     if (seg != a.nseg - 1)
         return;
-    float *Sout = a.S + head * kD * kD;
-    float *zout = a.z + head * kD;
+    float *Sout = a.S + head * kD * kD;  // the final z leaves from the producers
 #pragma unroll
     for (int tf = 0; tf < 8; ++tf)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             Sout[(tf * 16 + lg4 * 4 + r) * kD + cw] = sacc[tf][r];
-    if (lr == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            zout[fw + r] = zr[r];
-    }
 }
 
 // ============================================================================ pass 3, chunk 128
@@ -719,7 +749,8 @@ struct alignas(16) P8Smem {
     alignas(16) bf16 Vs[kP8C * kRow];  // v
     alignas(16) bf16 Kw[kP8C * kRow];  // write weights w phi(k), 0 past the end of the segment
     alignas(16) uint2 P[Cfg<kP8C>::NPT * 64];  // bf16 score tile (tj, ti) at tj (tj + 1) / 2 + ti
-    alignas(16) float zs[2][kD];       // z entering the chunk, by chunk parity
+    alignas(16) bf16 zhl[2][2][kD];    // z entering the chunk in bf16 high and low parts, by parity
+    alignas(16) float zred[3][kD];     // fp32 z update of the chunk from producer waves 9-11
     alignas(16) float dq[kP8C];        // phi(q_j) . z_prev
     alignas(16) float lg[2][kP8C];
     alignas(16) float gj[2][kP8C];
@@ -764,6 +795,15 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
         const int ld_off = tg * TPT * kD * 2 + fg * 16;
         uint4 rq[TPT], rk[TPT], rv[TPT];
         float ar[2] = {0.f, 0.f};  // alpha of the next chunk to scan: tokens lane, 64 + lane
+        // z: lanes 0-15 of wave 8 hold features 8 lane .. 8 lane + 7; each chunk adds the sum
+        // of its fp32 write weights w phi(k), formed before their rounding to bf16
+        float zreg[8], zsum[8];
+        if (wave == 8 && lane < 16) {
+            const float *zin = a.nseg == 1 ? a.z + head * kD : slot_ptr(a, head, seg) + kD * kD;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                zreg[e] = zin[8 * lane + e];
+        }
 
         auto load = [&](const rsrc_t &r, int c, uint4 (&x)[TPT]) {
 #pragma unroll
@@ -823,6 +863,9 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
         // 0 past the end of the segment)
         auto stage_vw = [&](int gs, int n) {
 #pragma unroll
+            for (int e = 0; e < 8; ++e)
+                zsum[e] = 0.f;
+#pragma unroll
             for (int p = 0; p < TPT; ++p) {
                 const int j = tg * TPT + p;
                 *reinterpret_cast<uint4 *>(&sm.Vs[pr_off(j, fg * 8)]) = rv[p];
@@ -831,9 +874,40 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
                 unpack8(rk[p], x);
                 bf16x8 kwb;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    kwb[e] = static_cast<bf16>(w * phi<FM>(x[e]));
+                for (int e = 0; e < 8; ++e) {
+                    const float wf = w * phi<FM>(x[e]);
+                    kwb[e] = static_cast<bf16>(wf);
+                    zsum[e] += wf;
+                }
                 *reinterpret_cast<bf16x8 *>(&sm.Kw[pr_off(j, fg * 8)]) = kwb;
+            }
+            // the wave's four token groups (lanes 16 t + fg) summed into every lane, in a
+            // fixed order; waves 9-11 hand theirs to wave 8 through sm.zred
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                zsum[e] += __shfl_xor(zsum[e], 16, 64);
+                zsum[e] += __shfl_xor(zsum[e], 32, 64);
+            }
+            if (wave > 8 && lane < 16) {
+                *reinterpret_cast<f32x4 *>(&sm.zred[wave - 9][8 * lane]) = f32x4{zsum[0], zsum[1], zsum[2], zsum[3]};
+                *reinterpret_cast<f32x4 *>(&sm.zred[wave - 9][8 * lane + 4]) = f32x4{zsum[4], zsum[5], zsum[6], zsum[7]};
+            }
+        };
+        // after stage_vw(c) and a barrier: z entering chunk c + 1, for part A of that chunk
+        auto z_update = [&](int c) {
+            if (wave == 8 && lane < 16) {
+                const float g = GATED ? sm.gj[c & 1][chunk_len(c) - 1] : 1.f;
+                bf16x8 zh, zl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float dz = zsum[e] + sm.zred[0][8 * lane + e] + sm.zred[1][8 * lane + e] +
+                                     sm.zred[2][8 * lane + e];
+                    zreg[e] = g * zreg[e] + dz;
+                    zh[e] = static_cast<bf16>(zreg[e]);
+                    zl[e] = static_cast<bf16>(zreg[e] - static_cast<float>(zh[e]));
+                }
+                *reinterpret_cast<bf16x8 *>(&sm.zhl[(c + 1) & 1][0][8 * lane]) = zh;
+                *reinterpret_cast<bf16x8 *>(&sm.zhl[(c + 1) & 1][1][8 * lane]) = zl;
             }
         };
 
@@ -856,12 +930,18 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
             load(rK, c + 1, rk);
             wg_barrier();  // a | b
             // part B of chunk c
+            z_update(c);
             if (c + 1 < n_chunks)
                 scan(chunk_len(c + 1), (c + 1) & 1);
             load_a(c + 2);
             stage_qk();
             load(rQ, c + 2, rq);
             wg_barrier();  // chunk c done
+        }
+        if (seg == a.nseg - 1 && wave == 8 && lane < 16) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                a.z[head * kD + 8 * lane + e] = zreg[e];
         }
         return;
     }
@@ -871,8 +951,7 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         ones[e] = static_cast<bf16>(1.f);
-    f32x4 sacc[8];
-    f32x4 zr;
+    f32x4 sacc[8];  // z lives with the producers, which pass each chunk's entering z through sm.zhl
     const int cw = wave * 16 + lr;
     const int fw = wave * 16 + lg4 * 4;
     {
@@ -883,11 +962,8 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 sacc[tf][r] = Sin[(tf * 16 + lg4 * 4 + r) * kD + cw];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            zr[r] = zin[fw + r];
         if (tid < kD)
-            sm.zs[0][tid] = zin[tid];
+            split_store(zin[tid], &sm.zhl[0][0][tid], &sm.zhl[0][1][tid]);
     }
     const rsrc_t rY = make_rsrc(a.Y + row0 * kD, len * kD * 2);
     // transposing-load addresses: this lane supplies 4 adjacent columns (4 (lr & 3) ..)
@@ -928,17 +1004,13 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
             const int j = wave * 16 + lr;
 #pragma unroll
             for (int kf = 0; kf < 4; ++kf) {
-                const f32x4 zlo = *reinterpret_cast<const f32x4 *>(&sm.zs[buf][kf * 32 + lg4 * 4]);
-                const f32x4 zhi = *reinterpret_cast<const f32x4 *>(&sm.zs[buf][kf * 32 + 16 + lg4 * 4]);
-                bf16x8 zb;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    zb[r] = static_cast<bf16>(zlo[r]);
-                    zb[4 + r] = static_cast<bf16>(zhi[r]);
-                }
+                bf16x8 zh, zl;  // z_prev in bf16 high and low parts
+                z_operand(sm.zhl[buf], kf * 32 + lg4 * 4, zh, zl);
                 const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&sm.Qs[pr_off(j, kf * 32 + lg4 * 4)]);
                 const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&sm.Qs[pr_off(j, opaque(kf * 32 + 16 + lg4 * 4))]);
-                d = mfma(zb, cat8(lo, hi), d);
+                const bf16x8 qv = cat8(lo, hi);
+                d = mfma(zh, qv, d);
+                d = mfma(zl, qv, d);
             }
         }
         for (int k = wave; k < G::NPT; k += 8) {
@@ -1041,9 +1113,6 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sacc[tf][r] *= g_end;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                zr[r] *= g_end;
         }
         // (4) in k order: lane group lg4 takes tokens 8lg4 + 2e (first load) and
         //     8lg4 + 2e + 1 (second) of each 32-token step, alike for both operands
@@ -1055,34 +1124,19 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
             for (int tf = 0; tf < 8; ++tf) {
                 const bf16x8 ka = cat8(ld_tr(&sm.Kw[pr_off(tb, tf * 16 + tc)]), ld_tr(&sm.Kw[pr_off(tb + 1, tf * 16 + tc)]));
                 sacc[tf] = mfma(ka, vb, sacc[tf]);
-                if (!GATED && tf == wave)  // this wave's features of z: the tile just loaded
-                    zr = mfma(ka, ones, zr);
-            }
-            if constexpr (GATED) {
-                // the gated instance measured faster with its own load of the z operand
-                const bf16x8 kz = cat8(ld_tr(&sm.Kw[pr_off(tb, wave * 16 + tc)]), ld_tr(&sm.Kw[pr_off(tb + 1, wave * 16 + tc)]));
-                zr = mfma(kz, ones, zr);
             }
         }
-        if (lr == 0)
-            *reinterpret_cast<f32x4 *>(&sm.zs[buf ^ 1][fw]) = zr;
         wg_barrier();  // chunk c done
     }
 
     if (seg != a.nseg - 1)
         return;
-    float *Sout = a.S + head * kD * kD;
-    float *zout = a.z + head * kD;
+    float *Sout = a.S + head * kD * kD;  // the final z leaves from the producers
 #pragma unroll
     for (int tf = 0; tf < 8; ++tf)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             Sout[(tf * 16 + lg4 * 4 + r) * kD + cw] = sacc[tf][r];
-    if (lr == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            zout[fw + r] = zr[r];
-    }
 }
 
 // ============================================================================ pass 1, chunk 64
@@ -1096,6 +1150,7 @@ template <bool GATED>
 struct alignas(16) SumSmem {
     alignas(16) bf16 Ws[2][kPcC * kRow];  // w phi(k) (ungated: phi(k), zero past the end)
     alignas(16) bf16 Vs[2][kPcC * kRow];
+    alignas(16) float zred[2][kSumProducers * 4][kD];  // fp32 z update per token group, by chunk parity
     alignas(16) float lg[3][kPcC];
     alignas(16) float gj[3][kPcC];
     alignas(16) int zp[3][kPcC];
@@ -1170,7 +1225,10 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                 sm.gj[gs][lane] = zf >= 0 ? 0.f : __expf(s);
             }
         };
+        // write weights w phi(k) in bf16 (Ws, the operand of S), 0 past the end of the
+        // segment, and their fp32 sums over this thread's tokens for z (zred)
         auto stage = [&](int buf, int gs, int n, const uint4 (&rkx)[TPT], const uint4 (&rvx)[TPT]) {
+            float zp8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int p = 0; p < TPT; ++p) {
                 const int j = tg * TPT + p;
@@ -1179,14 +1237,16 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                 unpack8(rkx[p], x);
                 bf16x8 kb;
 #pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    kb[s] = static_cast<bf16>(GATED ? w * phi<FM>(x[s]) : phi<FM>(x[s]));
-                uint4 u = *reinterpret_cast<uint4 *>(&kb);
-                if (!GATED && j >= n)
-                    u = make_uint4(0u, 0u, 0u, 0u);
-                *reinterpret_cast<uint4 *>(&sm.Ws[buf][pr_off(j, fg * 8)]) = u;
+                for (int s = 0; s < 8; ++s) {
+                    const float wf = GATED ? w * phi<FM>(x[s]) : (j < n ? phi<FM>(x[s]) : 0.f);
+                    kb[s] = static_cast<bf16>(wf);
+                    zp8[s] += wf;
+                }
+                *reinterpret_cast<uint4 *>(&sm.Ws[buf][pr_off(j, fg * 8)]) = *reinterpret_cast<uint4 *>(&kb);
                 *reinterpret_cast<uint4 *>(&sm.Vs[buf][pr_off(j, fg * 8)]) = rvx[p];
             }
+            *reinterpret_cast<f32x4 *>(&sm.zred[buf][tg][fg * 8]) = f32x4{zp8[0], zp8[1], zp8[2], zp8[3]};
+            *reinterpret_cast<f32x4 *>(&sm.zred[buf][tg][fg * 8 + 4]) = f32x4{zp8[4], zp8[5], zp8[6], zp8[7]};
         };
         // interval i: stage chunk i + 1 from its set and refill the set with chunk
         // i + 1 + kSumSets; scan the gates of chunk i + 2 and load the alpha of chunk i + 4
@@ -1228,18 +1288,13 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
     }
 
     // ================================================================ consumers
-    bf16x8 ones;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-        ones[s] = static_cast<bf16>(1.f);
     f32x4 sacc[8];
 #pragma unroll
     for (int tf = 0; tf < 8; ++tf)
         sacc[tf] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 zr = {0.f, 0.f, 0.f, 0.f};
+    float zf = 0.f;  // threads tid < 128: z of feature tid, from the producers' fp32 sums
     float g_seg = 1.f;
     const int cw = wave * 16 + lr;
-    const int fw = wave * 16 + lg4 * 4;
     const int te = lr >> 2, tc = 4 * (lr & 3);
     wg_barrier();
     wg_barrier();
@@ -1259,9 +1314,14 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sacc[tf][r] *= g_end;
+            zf *= g_end;
+        }
+        if (tid < kD) {
+            float dz = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                zr[r] *= g_end;
+            for (int t = 0; t < kSumProducers * 4; ++t)
+                dz += sm.zred[buf][t][tid];
+            zf += dz;
         }
 #pragma unroll
         for (int ki = 0; ki < G::NKI; ++ki) {
@@ -1272,8 +1332,6 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                 const bf16x8 ka = cat8(ld_tr(&Wb[pr_off(tb, tf * 16 + tc)]), ld_tr(&Wb[pr_off(tb + 1, tf * 16 + tc)]));
                 sacc[tf] = mfma(ka, vb, sacc[tf]);
             }
-            const bf16x8 kz = cat8(ld_tr(&Wb[pr_off(tb, wave * 16 + tc)]), ld_tr(&Wb[pr_off(tb + 1, wave * 16 + tc)]));
-            zr = mfma(kz, ones, zr);
         }
         wg_barrier();  // chunk i folded
     }
@@ -1296,11 +1354,8 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
             float *o = &Sout[(tf * 16 + lg4 * 4 + r) * kD + cw];
             *o = sacc[tf][r] + (add_in ? *o : 0.f);
         }
-    if (lr == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            zout[fw + r] = zr[r] + (add_in ? zout[fw + r] : 0.f);
-    }
+    if (tid < kD)
+        zout[tid] = zf + (add_in ? zout[tid] : 0.f);
 }
 
 // Pass 2: entering state of every segment, in place over the segment maps.

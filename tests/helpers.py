@@ -18,9 +18,12 @@ F32_REL = 1e-4          # fp32 inputs: outputs and final S/z
 BF16_Y_ABS = 2e-2       # bf16 inputs: outputs
 BF16_STATE_REL = 1e-2   # bf16 inputs: final S/z
 BF16_U = 2.0 ** -8      # unit roundoff of bf16 under round-to-nearest
-# z sums the bf16-rounded write weights w phi(k) that also feed S; every term is
-# positive, so z's relative error is at most BF16_U plus the fp32 accumulation
-Z_SUM_REL = BF16_U + 6e-4
+# Internal bounds, tighter than the bars above.  z accumulates the write weights w phi(k)
+# in fp32 before they are rounded to bf16 for S, so only fp32 accumulation separates it
+# from the exact sum of positive terms.  The outputs' per-head max-norm relative error is
+# flagged above 1e-2 (observed: a few 1e-3, from bf16 operands of relative error 2^-9).
+Z_REL = 1e-5
+Y_MAXNORM_REL = 1e-2
 
 
 def to_f64(t) -> np.ndarray:
