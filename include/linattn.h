@@ -77,7 +77,12 @@ typedef enum la_dtype {
  *                       Recurrent State", Step 4: its positive feature map)
  *   LA_PHI_RELU_EPS     max(x, 0) + 1e-5    (page "线性注意力架构演进", ai-master.cc: the
  *   LA_PHI_SIGMOID_EPS  sigmoid(x) + 1e-5    feature-map switch of its pluggable module)
- * All four are strictly positive for finite x, so the denominator stays positive.
+ * In exact arithmetic all four are strictly positive for finite x.  In the arithmetic type
+ * (fp32 for bf16 and f32 io, fp64 for f64 io) ELU(x) + 1 = exp(x) underflows to 0 for x
+ * below about -87 (fp32; -708 in fp64), while the other three never fall below 1e-5.  With
+ * eps = 0, a query whose every feature maps to 0 then reads 0 / 0 = NaN where exact
+ * arithmetic gives a finite value; with eps > 0 its output is 0, within rounding of the
+ * exact value.  Inputs that can reach that range should use eps > 0.
  */
 typedef enum la_feature_map {
     LA_PHI_ELU1 = 0,

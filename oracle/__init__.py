@@ -19,8 +19,8 @@ Source of truth is the page "Linear attention：把历史写进状态"
   [a2*a3, a3, 1]).  Brute force; an independent formula used to pin the
   recurrence.
 * :func:`chunkwise` -- the chunk equations of section "一个 chunk 的输出由两部分
-  组成", with the gated extension the page asks for ("门控版本要加入门乘积")
-  written as explicit gate products.
+  组成", with the gated extension that the page leaves open (it only says that
+  the gated form needs the gate products) written as explicit gate products.
 * :func:`scan_prefix` -- the affine composition (a2, B2) o (a1, B1) =
   (a2 a1, a2 B1 + B2) of section "门控递推为什么能做并行 scan", combined in
   tree order.

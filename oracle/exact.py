@@ -69,3 +69,27 @@ def delta_exact(q, k, v, beta, S0):
         preds.append(p)
         errs.append(e)
     return ys, Ss, preds, errs
+
+
+def relu1_exact(x) -> Fraction:
+    """max(x, 0) + 1 in rationals (the positive feature map of the datawhalechina chapter
+    "Linear Attention and Recurrent State", Step 4)."""
+    x = _frac(x)
+    return (x if x > 0 else Fraction(0)) + 1
+
+
+def noncausal_exact(qf, kf, v, eps=0):
+    """The non-causal form in rationals, from a zero state: S = sum of k~ v^T and
+    z = sum of k~ over every token, then y_t = q~_t^T S / (q~_t^T z + eps) for every t.
+    Returns ``(ys, S, z)``."""
+    r, dv = len(kf[0]), len(v[0])
+    eps = _frac(eps)
+    S = [[sum((_frac(kf[t][i]) * _frac(v[t][j]) for t in range(len(kf))), Fraction(0)) for j in range(dv)]
+         for i in range(r)]
+    z = [sum((_frac(kf[t][i]) for t in range(len(kf))), Fraction(0)) for i in range(r)]
+    ys = []
+    for q_t in qf:
+        q_t = [_frac(x) for x in q_t]
+        den = sum((q_t[i] * z[i] for i in range(r)), Fraction(0))
+        ys.append([sum((q_t[i] * S[i][j] for i in range(r)), Fraction(0)) / (den + eps) for j in range(dv)])
+    return ys, S, z

@@ -203,15 +203,19 @@ def _prefill_shapes(Q, K, V, Y, S, z):
     return B, H, T, d, dv
 
 
-def la_prefill_chunked_fm(Q, K, V, alpha, eps: float, chunk: int, Y, S, z, phi="elu1", stream=None) -> None:
-    """:func:`la_prefill_chunked` with the feature map ``phi`` (a FEATURE_MAPS name or code)."""
+def _gated_prefill_args(Q, K, V, alpha, Y, S, z):
+    """Shape and dtype checks of the causal prefill calls: (B, H, T, d, dv, io, st, ptrs)."""
     B, H, T, d, dv = _prefill_shapes(Q, K, V, Y, S, z)
     if alpha is not None and tuple(alpha.shape) != (B, H, T):
         raise ValueError("alpha must be [B, H, T]")
     _same_dtype("Q, K, V, Y", (Q, K, V, Y))
     _same_dtype("S, z, alpha", (S, z, alpha))
-    io, st = _dtype_code(Q), _dtype_code(S)
-    ptrs = _device_ptrs(Q, K, V, alpha, Y, S, z)
+    return B, H, T, d, dv, _dtype_code(Q), _dtype_code(S), _device_ptrs(Q, K, V, alpha, Y, S, z)
+
+
+def la_prefill_chunked_fm(Q, K, V, alpha, eps: float, chunk: int, Y, S, z, phi="elu1", stream=None) -> None:
+    """:func:`la_prefill_chunked` with the feature map ``phi`` (a FEATURE_MAPS name or code)."""
+    B, H, T, d, dv, io, st, ptrs = _gated_prefill_args(Q, K, V, alpha, Y, S, z)
     rc = library().la_prefill_chunked_fm(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, B, H, T, d, dv, float(eps),
                                          int(chunk), ptrs[4], ptrs[5], ptrs[6], st, _phi_code(phi),
                                          _stream_ptr(Q, stream))
@@ -240,25 +244,27 @@ def la_prefill_chunked(Q, K, V, alpha, eps: float, chunk: int, Y, S, z, stream=N
     Q, K: [B, H, T, d]; V, Y: [B, H, T, dv] (one io dtype); alpha: [B, H, T] or None;
     S: [B, H, d, dv], z: [B, H, d] (state dtype: float32 for bf16/f32 io, float64 for f64 io).
     """
-    if Q.dim() != 4 or tuple(K.shape) != tuple(Q.shape):
-        raise ValueError("Q and K must both be [B, H, T, d] with the same shape")
-    B, H, T, d = Q.shape
-    if V.dim() != 4 or tuple(V.shape[:3]) != (B, H, T):
-        raise ValueError("V must be [B, H, T, dv] with Q's B, H, T")
-    dv = V.shape[3]
-    if tuple(Y.shape) != tuple(V.shape):
-        raise ValueError("Y must have V's shape")
-    if tuple(S.shape) != (B, H, d, dv) or tuple(z.shape) != (B, H, d):
-        raise ValueError("S must be [B, H, d, dv] and z [B, H, d]")
-    if alpha is not None and tuple(alpha.shape) != (B, H, T):
-        raise ValueError("alpha must be [B, H, T]")
-    _same_dtype("Q, K, V, Y", (Q, K, V, Y))
-    _same_dtype("S, z, alpha", (S, z, alpha))
-    io, st = _dtype_code(Q), _dtype_code(S)
-    ptrs = _device_ptrs(Q, K, V, alpha, Y, S, z)
+    B, H, T, d, dv, io, st, ptrs = _gated_prefill_args(Q, K, V, alpha, Y, S, z)
     rc = library().la_prefill_chunked(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, B, H, T, d, dv, float(eps),
                                       int(chunk), ptrs[4], ptrs[5], ptrs[6], st, _stream_ptr(Q, stream))
     _check(rc, "la_prefill_chunked")
+
+
+def _decode_args(q, k, v, alpha, y, S, z):
+    """Shape and dtype checks of the decode calls: (N, d, dv, io, st, ptrs)."""
+    if q.dim() != 2 or tuple(k.shape) != tuple(q.shape):
+        raise ValueError("q and k must both be [N, d] with the same shape")
+    N, d = q.shape
+    if v.dim() != 2 or v.shape[0] != N:
+        raise ValueError("v must be [N, dv] with q's N")
+    dv = v.shape[1]
+    if tuple(y.shape) != (N, dv) or tuple(S.shape) != (N, d, dv) or tuple(z.shape) != (N, d):
+        raise ValueError("y must be [N, dv], S [N, d, dv] and z [N, d]")
+    if alpha is not None and tuple(alpha.shape) != (N,):
+        raise ValueError("alpha must be [N]")
+    _same_dtype("q, k, v, y", (q, k, v, y))
+    _same_dtype("S, z, alpha", (S, z, alpha))
+    return N, d, dv, _dtype_code(q), _dtype_code(S), _device_ptrs(q, k, v, alpha, y, S, z)
 
 
 def la_decode_step(q, k, v, alpha, eps: float, y, S, z, stream=None) -> None:
@@ -266,20 +272,7 @@ def la_decode_step(q, k, v, alpha, eps: float, y, S, z, stream=None) -> None:
 
     q, k: [N, d]; v, y: [N, dv]; alpha: [N] or None; S: [N, d, dv]; z: [N, d].
     """
-    if q.dim() != 2 or tuple(k.shape) != tuple(q.shape):
-        raise ValueError("q and k must both be [N, d] with the same shape")
-    N, d = q.shape
-    if v.dim() != 2 or v.shape[0] != N:
-        raise ValueError("v must be [N, dv] with q's N")
-    dv = v.shape[1]
-    if tuple(y.shape) != (N, dv) or tuple(S.shape) != (N, d, dv) or tuple(z.shape) != (N, d):
-        raise ValueError("y must be [N, dv], S [N, d, dv] and z [N, d]")
-    if alpha is not None and tuple(alpha.shape) != (N,):
-        raise ValueError("alpha must be [N]")
-    _same_dtype("q, k, v, y", (q, k, v, y))
-    _same_dtype("S, z, alpha", (S, z, alpha))
-    io, st = _dtype_code(q), _dtype_code(S)
-    ptrs = _device_ptrs(q, k, v, alpha, y, S, z)
+    N, d, dv, io, st, ptrs = _decode_args(q, k, v, alpha, y, S, z)
     rc = library().la_decode_step(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, N, d, dv, float(eps),
                                   ptrs[4], ptrs[5], ptrs[6], st, _stream_ptr(q, stream))
     _check(rc, "la_decode_step")
@@ -287,20 +280,7 @@ def la_decode_step(q, k, v, alpha, eps: float, y, S, z, stream=None) -> None:
 
 def la_decode_step_fm(q, k, v, alpha, eps: float, y, S, z, phi="elu1", stream=None) -> None:
     """:func:`la_decode_step` with the feature map ``phi`` (a FEATURE_MAPS name or code)."""
-    if q.dim() != 2 or tuple(k.shape) != tuple(q.shape):
-        raise ValueError("q and k must both be [N, d] with the same shape")
-    N, d = q.shape
-    if v.dim() != 2 or v.shape[0] != N:
-        raise ValueError("v must be [N, dv] with q's N")
-    dv = v.shape[1]
-    if tuple(y.shape) != (N, dv) or tuple(S.shape) != (N, d, dv) or tuple(z.shape) != (N, d):
-        raise ValueError("y must be [N, dv], S [N, d, dv] and z [N, d]")
-    if alpha is not None and tuple(alpha.shape) != (N,):
-        raise ValueError("alpha must be [N]")
-    _same_dtype("q, k, v, y", (q, k, v, y))
-    _same_dtype("S, z, alpha", (S, z, alpha))
-    io, st = _dtype_code(q), _dtype_code(S)
-    ptrs = _device_ptrs(q, k, v, alpha, y, S, z)
+    N, d, dv, io, st, ptrs = _decode_args(q, k, v, alpha, y, S, z)
     rc = library().la_decode_step_fm(ptrs[0], ptrs[1], ptrs[2], ptrs[3], io, N, d, dv, float(eps),
                                      ptrs[4], ptrs[5], ptrs[6], st, _phi_code(phi), _stream_ptr(q, stream))
     _check(rc, "la_decode_step_fm")

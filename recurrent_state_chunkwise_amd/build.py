@@ -37,23 +37,22 @@ def hipcc() -> str:
     return exe
 
 
-def _compile(src: str, build_dir: str, extra) -> str:
+def _compile(src: str, build_dir: str) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))
     return obj
 
 
-def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
-    """Compile and link; `extra_flags` (e.g. -D tuning constants) and `out` allow
-    alternative builds of the same sources."""
-    build_dir = BUILD if out == LIB else out + ".objs"
-    os.makedirs(build_dir, exist_ok=True)
+def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip for gfx950 and link liblinattn.so into the package."""
+    out = LIB
+    os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir, list(extra_flags)), srcs))
+        objs = list(ex.map(lambda s: _compile(s, BUILD), srcs))
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

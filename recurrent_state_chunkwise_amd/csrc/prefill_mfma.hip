@@ -6,11 +6,11 @@
 //   numerator   = Q~c S_prev + [(Q~c K~c^T) . M] Vc
 //   denominator = Q~c z_prev + rowsum[(Q~c K~c^T) . M]
 //   S_next = S_prev + K~c^T Vc,   z_next = z_prev + sum of the rows of K~c
-// and y = numerator / (denominator + eps).  The gate of section "加一个门" enters as the
-// page asks ("门控版本要加入门乘积"): with L_j the sum of log(alpha) over the chunk up to
-// token j, score (j, i) is weighted by exp(L_j - L_i), the read of S_prev and z_prev by
-// exp(L_j), the write of token i by exp(L_last - L_i) and the carried state by
-// exp(L_last); a zero gate inside (i, j] makes the weight exactly 0.
+// and y = numerator / (denominator + eps).  The gate of section "加一个门" enters through
+// gate products, which the page names without a formula: with L_j the sum of log(alpha)
+// over the chunk up to token j, score (j, i) is weighted by exp(L_j - L_i), the read of
+// S_prev and z_prev by exp(L_j), the write of token i by exp(L_last - L_i) and the
+// carried state by exp(L_last); a zero gate inside (i, j] makes the weight exactly 0.
 //
 // Parallel structure.  A sequence is cut into segments.  Because one gated update is
 // the affine map S -> a S + k~ v^T and such maps compose associatively (section "门控
@@ -50,13 +50,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;          // feature width d = r and value width dv
 constexpr float kLog2e = 1.4426950408889634f;
 
-// (sequence, segment) workgroups aimed for, per chunk size: one or two per compute unit
-#ifndef LA_SEGMENT_TARGET_C64
-#define LA_SEGMENT_TARGET_C64 256
-#endif
-#ifndef LA_SEGMENT_TARGET_C128
-#define LA_SEGMENT_TARGET_C128 256
-#endif
+// (sequence, segment) workgroups aimed for: one per compute unit (more segments, two
+// rounds of workgroups, measured slower)
+constexpr int64_t kSegmentTarget = 256;
 
 // per-(sequence, segment) slot in Y: S [128][128], z [128], segment gate product, pad
 constexpr int kSlotFloats = kD * kD + kD + 4;
@@ -241,24 +237,14 @@ __device__ __forceinline__ float *slot_ptr(const Args &a, int64_t head, int p)
 // so the two 8-byte halves of a (2) operand are kept from being fused.
 constexpr int kPcC = 64;
 constexpr int kPcConsumers = 512;
-// producer waves of the output pass (4 or 8)
-#ifndef LA_PC_PRODUCERS
-#define LA_PC_PRODUCERS 4
-#endif
-constexpr int kPcProducers = LA_PC_PRODUCERS;
-static_assert(kPcProducers == 4 || kPcProducers == 8, "4 or 8 producer waves");
+// Producer waves: 4 in the output pass (8 measured slower), 8 in the segment-map pass,
+// whose consumers only fold and whose registers fit 16 waves; the segment-map producers
+// keep 2 chunks of K and V in flight per thread (4 measured no faster).
+constexpr int kPcProducers = 4;
 constexpr int kPcThreads = kPcConsumers + 64 * kPcProducers;
-#ifndef LA_SUM_PRODUCERS
-#define LA_SUM_PRODUCERS 8
-#endif
-constexpr int kSumProducers = LA_SUM_PRODUCERS;  // producer waves of the segment-map pass
-static_assert(kSumProducers == 4 || kSumProducers == 8, "4 or 8 producer waves");
+constexpr int kSumProducers = 8;
 constexpr int kSumThreads = kPcConsumers + 64 * kSumProducers;
-#ifndef LA_SUM_SETS
-#define LA_SUM_SETS 2
-#endif
-constexpr int kSumSets = LA_SUM_SETS;  // chunks of K and V in flight per producer thread
-static_assert(kSumSets == 2 || kSumSets == 4, "2 or 4 register sets");
+constexpr int kSumSets = 2;
 
 constexpr int kRow = kD + 8;  // padded token row, in elements
 __device__ __forceinline__ int pr_off(int row, int col) { return row * kRow + col; }
@@ -1672,7 +1658,7 @@ hipError_t launch_noncausal_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
     a.z = static_cast<float *>(pa.z);
     a.T = pa.T;
     a.eps = (float)pa.eps;
-    const int64_t nseg = choose_segments(pa.T, pa.n_heads, kPcC, LA_SEGMENT_TARGET_C64);
+    const int64_t nseg = choose_segments(pa.T, pa.n_heads, kPcC, kSegmentTarget);
     const int64_t bph = (pa.T + kNcBlockTokens - 1) / kNcBlockTokens;
     if (nseg == 0 || pa.n_heads * bph > INT32_MAX)
         return hipErrorInvalidValue;
@@ -1696,10 +1682,8 @@ hipError_t launch_prefill_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
     a.T = pa.T;
     a.eps = (float)pa.eps;
 
-    // one or two resident workgroups per compute unit at chunk 64, one at chunk 128
     const int C = pa.chunk;
-    const int64_t nseg =
-        choose_segments(pa.T, pa.n_heads, C, C == 64 ? LA_SEGMENT_TARGET_C64 : LA_SEGMENT_TARGET_C128);
+    const int64_t nseg = choose_segments(pa.T, pa.n_heads, C, kSegmentTarget);
     if (nseg == 0)
         return hipErrorInvalidValue;
     a.nseg = (int)nseg;

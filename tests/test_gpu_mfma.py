@@ -1,7 +1,7 @@
 """GPU parity of the bf16 MFMA chunked prefill (d = dv = 128, chunk 64 or 128)
-against the FP64 oracle, through the C ABI: ragged lengths, every value-slice
-width the launcher picks, gates (including zero gates), carried state, the
-page's worked examples embedded at width 128, causality and chunk invariance."""
+against the FP64 oracle, through the C ABI: ragged lengths, one to many segments
+per sequence, gates (including zero gates), carried state, the page's worked
+examples embedded at width 128, causality and chunk invariance."""
 import math
 
 import numpy as np
@@ -71,7 +71,8 @@ def _check(Y, S, z, ref, label):
 
 
 CASES = [
-    # B, H, T, chunk, gated, with_state   (H*B picks the value-slice width: <64 -> 16, <128 -> 32, else 64)
+    # B, H, T, chunk, gated, with_state   (B*H and T set the segment count: one segment per
+    # sequence from 256 sequences up, up to 256 / (B*H) segments below)
     (1, 2, 1, 64, False, False),
     (1, 2, 63, 64, False, True),
     (1, 2, 200, 64, True, False),
@@ -245,3 +246,33 @@ def test_gated_walkthrough_at_width_128(torch):
         y = Y[0, 0, :, 0].float().cpu()
         for got, want in zip(y.tolist(), [2.0, 10 / 3, 6.0]):
             assert abs(got - want) <= 2.0 ** -8 * want
+
+
+@pytest.mark.parametrize("io,chunk", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_underflowing_query_row(torch, io, chunk):
+    """One query row of -200 in every feature: ELU+1 = exp(x) underflows to 0 in fp32 for all
+    of them.  With eps > 0 that output is exactly 0 (the FP64 value is below 1e-70); with
+    eps = 0 it is 0 / 0 = NaN, as linattn.h states.  Every other output keeps parity."""
+    B, H, T, j = 1, 2, 300, 77
+    g = torch.Generator(device="cuda")
+    g.manual_seed(515 + chunk)
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    mk = lambda: (torch.randn((B, H, T, D), generator=g, device="cuda") / math.sqrt(128)).to(dt)
+    Q, K, V = mk(), mk(), mk()
+    Q[:, :, j, :] = -200.0
+    others = [t for t in range(T) if t != j]
+    for eps in (1e-6, 0.0):
+        Y, S, z = _run(torch, Q, K, V, None, chunk, eps=eps)
+        Yr, Sr, zr, _ = oracle_prefill(Q, K, V, None, eps)
+        Yg = to_f64(Y)
+        if eps > 0:
+            assert (Yg[:, :, j] == 0).all() and np.abs(Yr[:, :, j]).max() < 1e-70
+        else:
+            assert np.isnan(Yg[:, :, j]).all()
+        assert np.isfinite(Yg[:, :, others]).all()
+        if io == "bf16":
+            assert max_abs(Yg[:, :, others], Yr[:, :, others]) <= BF16_Y_ABS
+            assert maxnorm_rel(to_f64(S), Sr, 2) <= 5e-3 and elem_rel(to_f64(z), zr) <= Z_REL
+        else:
+            assert maxnorm_rel(Yg[:, :, others], Yr[:, :, others], 2) <= 1e-4
+            assert maxnorm_rel(to_f64(S), Sr, 2) <= 1e-4 and elem_rel(to_f64(z), zr) <= 1e-4

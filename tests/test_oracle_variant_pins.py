@@ -93,7 +93,7 @@ def test_unknown_mode_rejected():
 
 
 def _pin_relu1_fixture_causal(recur):
-    fx = _load("p1_relu1_by_hand.json")
+    fx = _load("p1_relu1.json")
     inp = fx["inputs"]
     Y, S, z, _ = recur(np.array(inp["q"]), np.array(inp["k"]), np.array(inp["v"]), None, 0.0, None, None, "relu1")
     want = fx["causal"]
@@ -101,14 +101,14 @@ def _pin_relu1_fixture_causal(recur):
             and np.array_equal(z, _fl(want["z"])))
 
 
-def test_relu1_fixture_by_hand_causal():
+def test_relu1_fixture_causal():
     assert _pin_relu1_fixture_causal(oracle.recurrence)
 
 
 def test_relu1_fixture_contracts():
     # the chapter's own checks on its fixture: shapes, finiteness, positive normaliser,
     # earlier outputs unchanged when the last key and value move by +100
-    inp = _load("p1_relu1_by_hand.json")["inputs"]
+    inp = _load("p1_relu1.json")["inputs"]
     q, k, v = np.array(inp["q"]), np.array(inp["k"]), np.array(inp["v"])
     Y, S, z, _ = oracle.recurrence(q, k, v, None, 0.0, phi_mode="relu1")
     assert Y.shape == v.shape and S.shape == (2, 1) and z.shape == (2,)
@@ -147,7 +147,7 @@ def _pin_exercise1(nc):
 
 
 def _pin_relu1_fixture(nc):
-    fx = _load("p1_relu1_by_hand.json")
+    fx = _load("p1_relu1.json")
     inp = fx["inputs"]
     Y, S, z, _ = nc(np.array(inp["q"]), np.array(inp["k"]), np.array(inp["v"]), 0.0, None, None, "relu1")
     want = fx["noncausal"]
@@ -218,7 +218,7 @@ def test_noncausal_exercise1_reads_final_state():
     assert _pin_exercise1(_oracle_nc)
 
 
-def test_noncausal_relu1_fixture_by_hand():
+def test_noncausal_relu1_fixture():
     assert _pin_relu1_fixture(_oracle_nc)
 
 
@@ -348,3 +348,13 @@ def test_map_reference_mutant_passes():
 def test_map_planted_mistake_fails_a_pin(kind):
     f = _map_mutant(kind)
     assert not (_pin_closed_forms(f) and _pin_positive(f))
+
+
+def test_relu1_fixture_is_what_its_script_writes():
+    """p1_relu1.json is the output of tests/golden/make_p1_relu1.py (exact rationals, checked
+    against the values worked out by hand inside the script)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("make_p1_relu1", os.path.join(GOLDEN, "make_p1_relu1.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert _load("p1_relu1.json") == mod.build()
