@@ -1059,7 +1059,7 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
         // token tiles in pairs (2m, 2m + 1), both fed from each 32-token step's V^T operand:
         // tile 2m + 1 has m + 1 full pairs of score tiles, tile 2m has m full pairs and the
         // diagonal tile alone, taken in the last step
-#pragma unroll 1
+#pragma unroll
         for (int m = 0; m < G::NTJ / 2; ++m) {
             const int t0 = 2 * m, t1 = 2 * m + 1;
             const int kb0 = t0 * (t0 + 1) / 2, kb1 = t1 * (t1 + 1) / 2;
