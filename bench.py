@@ -388,32 +388,91 @@ def mix_ceiling(ceil, read_bytes, write_bytes):
     return (read_bytes + write_bytes) / t
 
 
-def cpu_baseline(wl, torch):
-    """The FP64 oracle on this host's cores, on a sample of the prefill workload."""
-    import oracle
-    import numpy as np
-    cfg = wl.PREFILL_UNGATED
-    threads = min(16, len(os.sched_getaffinity(0)))  # one GPU's share of the host
-    heads = cfg.B * cfg.H                             # the whole workload, ~15 CPU-seconds
-    Q, K, V, _ = wl.prefill_inputs(cfg, "cpu", B=1, H=heads)
-    f64 = lambda t: t.to(torch.float64).numpy()
-    q, k, v = f64(Q), f64(K), f64(V)
-    # the whole workload, repeated until about a second of wall time (10-30 CPU-seconds on
-    # a GPU's share of the host), at most five times
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _time_oracle(fn, min_s=0.5, max_reps=5):
+    """Mean wall seconds of fn() over repeats until about min_s (at least one, at most max_reps)."""
     reps, t0 = 0, time.perf_counter()
-    while reps < 5 and (reps == 0 or time.perf_counter() - t0 < 1.0):
-        oracle.recurrence_heads(q, k, v, eps=cfg.eps, threads=threads)
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_s):
+        fn()
         reps += 1
-    dt = (time.perf_counter() - t0) / reps
-    head_tokens = heads * cfg.T
+    return (time.perf_counter() - t0) / reps, reps
+
+
+def cpu_baseline(wl, torch):
+    """The FP64 oracle on this host's cores (one GPU's share: at most 16 threads), on the
+    workloads or bounded samples of them, inputs drawn on the host with the same recipes.
+    The headline entry is the ungated prefill workload in full; `configs` times every
+    workload, with the decode and long-sequence ones on samples and their full-workload
+    times extrapolated (states and heads are independent) and labelled as such."""
+    import numpy as np
+    import oracle
+    threads = min(16, len(os.sched_getaffinity(0)))
+    f64 = lambda t: t.to(torch.float64).numpy()
+    rows = []
+
+    def prefill_row(cfg, heads_total, H_sample, label):
+        Q, K, V, A = wl.prefill_inputs(cfg, "cpu", B=1, H=H_sample)
+        q, k, v = f64(Q), f64(K), f64(V)
+        a = None if A is None else f64(A)
+        th = min(threads, H_sample)
+        dt, reps = _time_oracle(lambda: oracle.recurrence_heads(q, k, v, a, eps=cfg.eps, threads=th))
+        rate = H_sample * cfg.T / dt  # head-tokens/s
+        row = {"workload": cfg.name, "sample": label, "threads": th, "runs": reps, "seconds_per_run": dt,
+               "head_tokens_per_s": rate}
+        if H_sample < heads_total:
+            # the remaining heads run on the same threads, th at a time
+            full = dt * heads_total / H_sample * th / min(threads, heads_total)
+            row["full_workload_seconds_extrapolated"] = full
+        else:
+            full = row["full_workload_seconds"] = dt
+        row["tokens_per_s"] = cfg.B * cfg.T / full  # of the whole workload, on `threads` threads
+        return row
+
+    cfg2 = wl.PREFILL_UNGATED
+    rows.append(prefill_row(wl.SINGLE_HEAD_F64, 1, 1, "the whole workload (1 head x 64 tokens, fp64)"))
+    rows.append(prefill_row(cfg2, cfg2.B * cfg2.H, cfg2.B * cfg2.H, "the whole workload (64 heads x 4096 tokens)"))
+    g3 = wl.PREFILL_GATED
+    rows.append(prefill_row(g3, g3.B * g3.H, g3.B * g3.H, "the whole workload (32 heads x 16384 tokens)"))
+    g5 = wl.PREFILL_LONG
+    rows.append(prefill_row(g5, g5.B * g5.H, 4, "4 of the 32 heads x 131072 tokens (extrapolated to 32 heads)"))
+    # decode: 2048 states seeded by 256 writes (untimed), then 128 of the 1024 steps timed
+    dcfg = wl.DECODE
+    n_s, n_steps = 2048, 128
+    ks, vs = wl.decode_seed_inputs(dcfg, "cpu", n_states=n_s)
+    _, S0, z0, _ = oracle.recurrence_heads(f64(ks), f64(ks), f64(vs), eps=dcfg.eps, threads=threads)
+    steps = [wl.decode_step_inputs(dcfg, i, "cpu", n_states=n_s) for i in range(n_steps)]
+    st = lambda j: np.stack([f64(x[j]) for x in steps], axis=1)[:, None]
+    q, k, v = st(0), st(1), st(2)
+    dt, reps = _time_oracle(lambda: oracle.recurrence_heads(q, k, v, eps=dcfg.eps, S0=S0[:, None], z0=z0[:, None],
+                                                            threads=threads))
+    rate = n_s * n_steps / dt
+    rows.append({"workload": dcfg.name, "sample": "2048 of the 65536 states x 128 of the 1024 steps, from states "
+                 "seeded by 256 writes (extrapolated to the whole workload)", "threads": threads, "runs": reps,
+                 "seconds_per_run": dt, "state_steps_per_s": rate,
+                 "full_workload_seconds_extrapolated": dcfg.n_states * dcfg.steps / rate})
+    main_row = rows[1]
     return {
-        "value": head_tokens / dt / cfg.H,
+        "value": main_row["tokens_per_s"],
         "unit": "tokens/s",
-        "cores": threads,
+        "cores": main_row["threads"],
         "kind": "oracle",
-        "sample": "all %d heads x %d tokens of the B=%d,H=%d,T=%d ungated workload, %d runs of %.2f s wall "
-                  "(inputs drawn on the host); tokens/s = head-tokens/s / H" % (heads, cfg.T, cfg.B, cfg.H, cfg.T,
-                                                                             reps, dt),
+        "sample": "all 64 heads x 4096 tokens of the B=4,H=16,T=4096 ungated workload, %d runs of %.2f s wall "
+                  "(inputs drawn on the host); tokens/s = head-tokens/s / H" % (main_row["runs"],
+                                                                             main_row["seconds_per_run"]),
+        "cpu_model": cpu_model(),
+        "threads_available": len(os.sched_getaffinity(0)),
+        "configs": rows,
     }
 
 

@@ -290,6 +290,25 @@ const char *la_status_str(la_status status);
 int32_t la_prefill_variant(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk,
                            int32_t gated, la_dtype state_dtype);
 
+/*
+ * How the bf16 MFMA prefill (d = dv = 128) cuts each of n_heads sequences of T tokens,
+ * without running anything: the plan la_prefill_chunked uses at chunk 64 or 128 and
+ * la_prefill_noncausal at 64.  Sequences are cut into segments so that the
+ * (sequence, segment) workgroups give every compute unit work; the state entering each
+ * segment follows from the segments before it by the associative composition of gated
+ * updates (section "门控递推为什么能做并行 scan").  Returns the number of segments per
+ * sequence and sets *seg_len to the length of every segment but the last, which takes
+ * the rest (*seg_len = T for one segment).  Every segment but the last is a whole number
+ * of chunks; with more than one segment, each segment is long enough to hold, in its own
+ * rows of Y, a slot of la_prefill_segment_slot_bytes() bytes where the state entering it
+ * is parked before its outputs overwrite those rows, and every segment stays below 2^31
+ * bytes of Q.  Returns 0 when n_heads x segments would not fit one launch (the prefill
+ * then fails with LA_ERR_LAUNCH) and -1 for seg_len NULL, n_heads or T < 1, or a chunk
+ * other than 64 or 128.
+ */
+int64_t la_prefill_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t *seg_len);
+int64_t la_prefill_segment_slot_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,6 +56,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "linattn_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liblinattn_oracle.so")
+# A build of the same source to load instead (the sanitizer test points this at a build
+# with AddressSanitizer and UndefinedBehaviorSanitizer); it must exist, nothing is built.
+_ALT_LIB = os.environ.get("LINATTN_ORACLE_LIB")
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
 
 PHI_ELU1 = 0
 PHI_IDENTITY = 1
@@ -86,12 +91,31 @@ def build_oracle(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_oracle_sanitized(path: str) -> str:
+    """Compile the same source with AddressSanitizer and UndefinedBehaviorSanitizer into
+    ``path`` (host code, gcc; loaded through LINATTN_ORACLE_LIB with libasan preloaded)."""
+    cmd = ["gcc", *SANITIZE_FLAGS, "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", path, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return path
+
+
+def loaded_library() -> str:
+    """Path of the oracle library this process uses."""
+    return _ALT_LIB or _LIB_PATH
+
+
 def _load():
     global _lib
     with _lib_lock:
         if _lib is None:
-            build_oracle(force=False)
-            lib = ctypes.CDLL(_LIB_PATH)
+            if _ALT_LIB:
+                if not os.path.exists(_ALT_LIB):
+                    raise RuntimeError("LINATTN_ORACLE_LIB names a missing file: %s" % _ALT_LIB)
+                lib = ctypes.CDLL(_ALT_LIB)
+            else:
+                build_oracle(force=False)
+                lib = ctypes.CDLL(_LIB_PATH)
             dp = ctypes.POINTER(ctypes.c_double)
             lib.oracle_recurrence.restype = ctypes.c_int
             lib.oracle_recurrence.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,

@@ -24,7 +24,8 @@ __all__ = [
     "la_state_init", "la_prefill_chunked", "la_prefill_chunked_fm", "la_prefill_noncausal", "la_decode_step",
     "la_decode_step_fm", "la_delta_decode_step", "la_softmax_decode_step", "la_softmax_decode_workspace_bytes",
     "la_softmax_decode_step_static", "LA_SOFTMAX_STATIC_WORKSPACE_BYTES",
-    "la_status_str", "la_prefill_variant", "library", "library_path",
+    "la_status_str", "la_prefill_variant", "la_prefill_segments", "la_prefill_segment_slot_bytes", "library",
+    "library_path",
 ]
 
 LA_F64, LA_F32, LA_BF16 = 0, 1, 2
@@ -108,6 +109,10 @@ def library() -> ctypes.CDLL:
                                                           f64, vp, vp]
             lib.la_softmax_decode_workspace_bytes.restype = i64
             lib.la_softmax_decode_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
+            lib.la_prefill_segments.restype = i64
+            lib.la_prefill_segments.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
+            lib.la_prefill_segment_slot_bytes.restype = i64
+            lib.la_prefill_segment_slot_bytes.argtypes = []
             lib.la_prefill_variant.restype = ctypes.c_int32
             lib.la_prefill_variant.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int]
             _lib = lib
@@ -369,3 +374,16 @@ def la_softmax_decode_step_static(q, k, v, pos: int, K_cache, V_cache, y, scale=
 def la_prefill_variant(io_dtype: int, d: int, dv: int, chunk: int, gated: bool, state_dtype: int) -> int:
     """1 = bf16 MFMA kernel, 0 = general kernel, -1 = rejected."""
     return int(library().la_prefill_variant(io_dtype, d, dv, chunk, int(bool(gated)), state_dtype))
+
+
+def la_prefill_segments(n_heads: int, T: int, chunk: int):
+    """(segments per sequence, length of all but the last) of the bf16 MFMA prefill's plan;
+    segments = 0 when the grid would not fit a launch, -1 for invalid arguments."""
+    seg_len = ctypes.c_int64(0)
+    n = int(library().la_prefill_segments(int(n_heads), int(T), int(chunk), ctypes.byref(seg_len)))
+    return n, int(seg_len.value)
+
+
+def la_prefill_segment_slot_bytes() -> int:
+    """Bytes of the state each segment after the first parks in its own rows of Y."""
+    return int(library().la_prefill_segment_slot_bytes())

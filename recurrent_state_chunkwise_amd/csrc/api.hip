@@ -194,6 +194,19 @@ int32_t la_prefill_variant(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chu
     return la::mfma_prefill_supported(io_dtype, d, dv, chunk) ? 1 : 0;
 }
 
+int64_t la_prefill_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t *seg_len)
+{
+    if (!seg_len || n_heads < 1 || T < 1 || (chunk != 64 && chunk != 128))
+        return -1;
+    int64_t nseg, len;
+    if (!la::plan_segments(n_heads, T, chunk, &nseg, &len))
+        return 0;
+    *seg_len = len;
+    return nseg;
+}
+
+int64_t la_prefill_segment_slot_bytes(void) { return la::segment_slot_bytes(); }
+
 la_status la_prefill_chunked_fm(const void *Q, const void *K, const void *V, const void *alpha, la_dtype io_dtype,
                                 int64_t B, int64_t H, int64_t T, int32_t d, int32_t dv, double eps, int32_t chunk,
                                 void *Y, void *S, void *z, la_dtype state_dtype, la_feature_map phi,

@@ -1633,6 +1633,17 @@ int64_t choose_segments(int64_t T, int64_t n_heads, int C, int64_t target)
 
 }  // namespace
 
+bool plan_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t *nseg, int64_t *seg_len)
+{
+    *nseg = choose_segments(T, n_heads, chunk, kSegmentTarget);
+    if (*nseg == 0)
+        return false;
+    *seg_len = *nseg == 1 ? T : ((T / *nseg) / chunk) * chunk;  // the last segment takes the rest
+    return true;
+}
+
+int64_t segment_slot_bytes() { return (int64_t)kSlotFloats * 4; }
+
 bool mfma_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk)
 {
     return io_dtype == LA_BF16 && d == kD && dv == kD && (chunk == 64 || chunk == 128);
@@ -1658,12 +1669,12 @@ hipError_t launch_noncausal_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
     a.z = static_cast<float *>(pa.z);
     a.T = pa.T;
     a.eps = (float)pa.eps;
-    const int64_t nseg = choose_segments(pa.T, pa.n_heads, kPcC, kSegmentTarget);
+    int64_t nseg, seg_len;
     const int64_t bph = (pa.T + kNcBlockTokens - 1) / kNcBlockTokens;
-    if (nseg == 0 || pa.n_heads * bph > INT32_MAX)
+    if (!plan_segments(pa.n_heads, pa.T, kPcC, &nseg, &seg_len) || pa.n_heads * bph > INT32_MAX)
         return hipErrorInvalidValue;
     a.nseg = (int)nseg;
-    a.seg_len = nseg == 1 ? pa.T : ((pa.T / nseg) / kPcC) * kPcC;  // the last segment takes the rest
+    a.seg_len = seg_len;
     return dispatch_feature_map(pa.phi, [&](auto fm) { return launch_nc<decltype(fm)::value>(a, pa.n_heads, stream); });
 }
 
@@ -1683,11 +1694,11 @@ hipError_t launch_prefill_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
     a.eps = (float)pa.eps;
 
     const int C = pa.chunk;
-    const int64_t nseg = choose_segments(pa.T, pa.n_heads, C, kSegmentTarget);
-    if (nseg == 0)
+    int64_t nseg, seg_len;
+    if (!plan_segments(pa.n_heads, pa.T, C, &nseg, &seg_len))
         return hipErrorInvalidValue;
     a.nseg = (int)nseg;
-    a.seg_len = nseg == 1 ? pa.T : ((pa.T / nseg) / C) * C;  // the last segment takes the rest
+    a.seg_len = seg_len;
 
     return dispatch_feature_map(pa.phi, [&](auto fm) {
         constexpr int FM = decltype(fm)::value;

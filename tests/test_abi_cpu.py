@@ -290,3 +290,54 @@ def test_softmax_decode_static_rejections(lib):
     need = la.la_softmax_decode_workspace_bytes(BF16, 4096, 8192, 128)
     assert need == 4096 * 32 * 130 * 4 > la.LA_SOFTMAX_STATIC_WORKSPACE_BYTES
     assert softmax_static(lib, **big) == WORKSPACE
+
+
+# ---------------------------------------------------------------- the segment plan
+PLAN_T = [1, 2, 63, 64, 65, 258, 259, 319, 320, 321, 383, 384, 385, 1000, 4096, 16384, 131072, 1 << 20,
+          (1 << 22) - 1, 1 << 22, (1 << 22) + 1, 1 << 23, (1 << 24) + 17, 3 * (1 << 24) + 5]
+PLAN_H = [1, 2, 3, 4, 31, 32, 64, 100, 255, 256, 257, 4096, 65536, 1 << 20, (1 << 31) - 1]
+INT32_MAX = (1 << 31) - 1
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_segment_plan_invariants(lib, chunk):
+    """The plan of the bf16 MFMA prefill at extreme lengths and head counts: whole chunks,
+    every segment's own rows of Y hold its state slot, 32-bit offsets inside a segment, a grid
+    that fits one launch, the compute units filled when the length allows, and no more
+    segments than needed."""
+    slot = la.la_prefill_segment_slot_bytes()
+    assert slot == (128 * 128 + 128 + 4) * 4  # S, z and the segment's gate product, padded
+    row = 128 * 2                              # bytes of one token's row of Q, K, V or Y
+    min_len = -(-(-(-slot // row)) // chunk) * chunk  # shortest segment that holds a slot
+    max_len = (1 << 31) // row // 2            # longest segment but the last: below 2^30 bytes
+    for T in PLAN_T:
+        for H in PLAN_H:
+            nseg, seg_len = la.la_prefill_segments(H, T, chunk)
+            if nseg == 0:  # refused: even the fewest segments would not fit one grid
+                assert H * -(-T // max_len) > INT32_MAX, (T, H)
+                continue
+            assert 1 <= nseg and H * nseg <= INT32_MAX, (T, H, nseg)
+            last = T - (nseg - 1) * seg_len
+            if nseg == 1:
+                assert seg_len == T and T * row < (1 << 31), (T, H)
+                continue
+            assert seg_len % chunk == 0 and seg_len >= min_len, (T, H, seg_len)
+            assert seg_len * row >= slot                 # slot p sits in segment p's own rows
+            assert seg_len <= last, (T, H, seg_len, last)  # the last segment takes the rest
+            assert last * row < (1 << 31) and seg_len * row < (1 << 31)
+            want = -(-256 // H)                          # workgroups to fill 256 compute units
+            if T // min_len >= want:
+                assert H * nseg >= 256 or nseg >= want, (T, H, nseg)
+            assert nseg <= max(want, -(-T // max_len)), (T, H, nseg)
+
+
+def test_segment_plan_rejections(lib):
+    assert la.la_prefill_segments(0, 100, 64)[0] == -1
+    assert la.la_prefill_segments(4, 0, 64)[0] == -1
+    assert la.la_prefill_segments(4, 100, 32)[0] == -1
+    assert lib.la_prefill_segments(4, 100, 64, None) == -1
+    # the full workloads: one segment per compute unit (or per sequence past 256 sequences)
+    assert la.la_prefill_segments(64, 4096, 64) == (4, 1024)
+    assert la.la_prefill_segments(32, 16384, 64) == (8, 2048)
+    assert la.la_prefill_segments(32, 131072, 128) == (8, 16384)
+    assert la.la_prefill_segments(65536, 256, 64) == (1, 256)

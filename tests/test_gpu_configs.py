@@ -172,3 +172,45 @@ def test_decode_full_config_sampled(torch):
     _report(cfg.name + " (2048 sampled states)", ya, yr, sr, zrel)
     assert ya <= BF16_Y_ABS and sr <= BF16_STATE_REL and zrel <= BF16_STATE_REL
     assert sr <= 1e-4 and zrel <= 1e-4 and yr <= 1e-2
+
+
+def test_numerics_protocol_long_heads(torch):
+    """The numerics check of the page "Linear attention：把历史写进状态" (section "长历史下，状态的
+    数值范围会增长": sweep the length, the input scale and the chunk, recording the largest
+    error and the smallest denominator).  Heads 0, 11, 22 and 31 of the long gated workload,
+    with Q, K and V scaled by 1, 4 and 16 (powers of two: exact in bf16), run at chunks 64
+    and 128 against the FP64 oracle on the same values.  Printed per run: the error of y per
+    window of positions [2^k, 2^(k+1)), the smallest denominator, and the final S and z."""
+    cfg = wl.PREFILL_LONG
+    Q, K, V, A = wl.prefill_inputs(cfg, "cuda")
+    idx = torch.tensor([0, 11, 22, 31], device="cuda")
+    Q4, K4, V4, A4 = (t[:, idx].contiguous() for t in (Q, K, V, A))
+    del Q, K, V, A
+    H = 4
+    for scale in (1, 4, 16):
+        Qs, Ks, Vs = (t * scale for t in (Q4, K4, V4))
+        Yr, Sr, zr, den = oracle.recurrence_heads(to_f64(Qs), to_f64(Ks), to_f64(Vs), to_f64(A4), eps=cfg.eps,
+                                                  threads=THREADS)
+        for chunk in (64, 128):
+            Y = torch.empty_like(Vs)
+            S = torch.empty((1, H, cfg.d, cfg.dv), device="cuda")
+            z = torch.empty((1, H, cfg.d), device="cuda")
+            la.la_state_init(S, z)
+            la.la_prefill_chunked(Qs, Ks, Vs, A4, cfg.eps, chunk, Y, S, z)
+            torch.cuda.synchronize()
+            Yg = to_f64(Y)
+            ya, yr = max_abs(Yg, Yr), maxnorm_rel(Yg, Yr, 2)
+            sr, zrel = maxnorm_rel(to_f64(S), Sr, 2), elem_rel(to_f64(z), zr)
+            err = np.abs(Yg - Yr).max(axis=(0, 1, 3))
+            wins = []
+            for k in range(18):
+                lo, hi = (1 << k) - 1, min((1 << (k + 1)) - 1, cfg.T)
+                if lo >= cfg.T:
+                    break
+                wins.append("%.1e" % err[lo:hi].max())
+            print("protocol scale x%-2d chunk %3d: y max abs %.2e  y max-norm rel %.2e  S rel %.2e  z rel %.2e"
+                  "  min den %.3e  max |y| %.2e" % (scale, chunk, ya, yr, sr, zrel, den.min(), np.abs(Yr).max()),
+                  flush=True)
+            print("  max |dy| per window [2^k - 1, 2^(k+1) - 1), k = 0..17: " + " ".join(wins), flush=True)
+            assert np.isfinite(Yg).all()
+            assert yr <= Y_MAXNORM_REL and sr <= BF16_STATE_REL and zrel <= Z_REL, (scale, chunk, yr, sr, zrel)
