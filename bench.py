@@ -42,6 +42,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix (and packed vector) peak
 STATE_BYTES = 128 * 128 * 4 + 128 * 4
 
 
@@ -78,8 +79,10 @@ def measured_traffic(kind):
     return None
 
 
-def prefill_bytes(B, H, T, gated):
-    return B * H * T * (1024 + (4 if gated else 0)) + 2 * B * H * STATE_BYTES
+def prefill_bytes(B, H, T, gated, io_bytes=2):
+    # Q, K, V read and Y written (4 x 128 elements per head-token in the io dtype), alpha (fp32)
+    # when gated, the fp32 state read and written once per head
+    return B * H * T * (512 * io_bytes + (4 if gated else 0)) + 2 * B * H * STATE_BYTES
 
 
 def prefill_useful_flops(B, H, T, C, d=128, dv=128):
@@ -483,7 +486,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the decode and gated workloads")
-    ap.add_argument("--only", choices=["prefill", "noncausal", "gated", "long", "decode", "delta", "kvstate", "copy"],
+    ap.add_argument("--only", choices=["prefill", "noncausal", "gated", "long", "fp32", "decode", "delta", "kvstate",
+                                       "copy"],
                     default=None,
                     help="run one workload only and print its timing (for profiler runs)")
     ap.add_argument("--decode-steps", type=int, default=None,
@@ -524,8 +528,8 @@ def main():
         print(json.dumps({"only": "kvstate", "kv_vs_state": time_kv_state(torch, la, wl, wl.KV_STATE),
                           "kv_vs_state_batched": time_kv_state(torch, la, wl, wl.KV_STATE_BATCHED)}))
         return
-    if args.only in ("gated", "long"):
-        ocfg = wl.PREFILL_GATED if args.only == "gated" else wl.PREFILL_LONG
+    if args.only in ("gated", "long", "fp32"):
+        ocfg = {"gated": wl.PREFILL_GATED, "long": wl.PREFILL_LONG, "fp32": wl.PREFILL_UNGATED_F32}[args.only]
         r = time_prefill(torch, la, wl, ocfg, args.steps, args.warmup)
         print(json.dumps({"only": args.only, "workload": ocfg.name, "steps": args.steps,
                           "ms_per_step": r["total_ms"] / args.steps, **r}))
@@ -635,6 +639,18 @@ def main():
             other.append({"workload": ocfg.name, "value": ocfg.B * ocfg.T / (o_call / 1e3), "unit": "tokens/s",
                           "call_ms": o_call, "hbm_frac": ob / (o_call / 1e3) / 1e9 / HBM_PEAK_GBS,
                           "mfma_frac": of / (o_call / 1e3) / 1e12 / BF16_PEAK_TFLOPS})
+        # the fp32-input path on the ungated shape: its useful flops at the fp32 matrix peak
+        # take longer than its bytes at the HBM peak, so that is its roofline
+        fcfg = wl.PREFILL_UNGATED_F32
+        f_call = time_prefill(torch, la, wl, fcfg, args.steps, args.warmup, sets=1)["call_ms"]
+        fb = prefill_bytes(fcfg.B, fcfg.H, fcfg.T, fcfg.gated, io_bytes=4)
+        ff = prefill_useful_flops(fcfg.B, fcfg.H, fcfg.T, fcfg.chunk)
+        other.append({"workload": fcfg.name, "value": fcfg.B * fcfg.T / (f_call / 1e3), "unit": "tokens/s",
+                      "call_ms": f_call, "dtype": "f32",
+                      "roofline": {"bound": "mfma", "achieved": ff / (f_call / 1e3) / 1e12, "peak": FP32_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": ff / (f_call / 1e3) / 1e12 / FP32_PEAK_TFLOPS,
+                                   "hbm_frac": fb / (f_call / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                   "algorithmic_bytes": fb, "useful_flops": ff}})
         out["other"] = other
     if not args.no_extra:
         ceil = measured_ceilings(torch)

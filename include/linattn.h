@@ -284,16 +284,17 @@ const char *la_status_str(la_status status);
 
 /*
  * Which prefill kernel a request would run, without running it:
- *   1 = bf16 MFMA chunked kernel, 0 = general kernel, -1 = the request is rejected
+ *   1 = bf16 MFMA chunked kernel (d = dv = 128, chunk 64 or 128), 2 = fp32 MFMA chunked
+ *   kernel (f32 io, d = dv = 128, chunk 64), 0 = general kernel, -1 = the request is rejected
  *   (the same checks as la_prefill_chunked on the scalar arguments).
  */
 int32_t la_prefill_variant(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk,
                            int32_t gated, la_dtype state_dtype);
 
 /*
- * How the bf16 MFMA prefill (d = dv = 128) cuts each of n_heads sequences of T tokens,
- * without running anything: the plan la_prefill_chunked uses at chunk 64 or 128 and
- * la_prefill_noncausal at 64.  Sequences are cut into segments so that the
+ * How the MFMA prefill (d = dv = 128; bf16 io at chunk 64 or 128, f32 io at chunk 64) cuts
+ * each of n_heads sequences of T tokens, without running anything: the plan
+ * la_prefill_chunked uses for those requests (la_prefill_noncausal: bf16 at 64).  Sequences are cut into segments so that the
  * (sequence, segment) workgroups give every compute unit work; the state entering each
  * segment follows from the segments before it by the associative composition of gated
  * updates (section "门控递推为什么能做并行 scan").  Returns the number of segments per
@@ -303,10 +304,10 @@ int32_t la_prefill_variant(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chu
  * rows of Y, a slot of la_prefill_segment_slot_bytes() bytes where the state entering it
  * is parked before its outputs overwrite those rows, and every segment stays below 2^31
  * bytes of Q.  Returns 0 when n_heads x segments would not fit one launch (the prefill
- * then fails with LA_ERR_LAUNCH) and -1 for seg_len NULL, n_heads or T < 1, or a chunk
- * other than 64 or 128.
+ * then fails with LA_ERR_LAUNCH) and -1 for seg_len NULL, n_heads or T < 1, or an
+ * (io_dtype, chunk) pair the MFMA prefill does not take.
  */
-int64_t la_prefill_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t *seg_len);
+int64_t la_prefill_segments(la_dtype io_dtype, int64_t n_heads, int64_t T, int32_t chunk, int64_t *seg_len);
 int64_t la_prefill_segment_slot_bytes(void);
 
 #ifdef __cplusplus

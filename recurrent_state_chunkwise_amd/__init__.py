@@ -110,7 +110,7 @@ def library() -> ctypes.CDLL:
             lib.la_softmax_decode_workspace_bytes.restype = i64
             lib.la_softmax_decode_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
             lib.la_prefill_segments.restype = i64
-            lib.la_prefill_segments.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
+            lib.la_prefill_segments.argtypes = [ctypes.c_int, i64, i64, i32, ctypes.POINTER(i64)]
             lib.la_prefill_segment_slot_bytes.restype = i64
             lib.la_prefill_segment_slot_bytes.argtypes = []
             lib.la_prefill_variant.restype = ctypes.c_int32
@@ -372,15 +372,15 @@ def la_softmax_decode_step_static(q, k, v, pos: int, K_cache, V_cache, y, scale=
 
 
 def la_prefill_variant(io_dtype: int, d: int, dv: int, chunk: int, gated: bool, state_dtype: int) -> int:
-    """1 = bf16 MFMA kernel, 0 = general kernel, -1 = rejected."""
+    """1 = bf16 MFMA kernel, 2 = fp32 MFMA kernel, 0 = general kernel, -1 = rejected."""
     return int(library().la_prefill_variant(io_dtype, d, dv, chunk, int(bool(gated)), state_dtype))
 
 
-def la_prefill_segments(n_heads: int, T: int, chunk: int):
-    """(segments per sequence, length of all but the last) of the bf16 MFMA prefill's plan;
+def la_prefill_segments(n_heads: int, T: int, chunk: int, io_dtype: int = LA_BF16):
+    """(segments per sequence, length of all but the last) of the MFMA prefill's plan;
     segments = 0 when the grid would not fit a launch, -1 for invalid arguments."""
     seg_len = ctypes.c_int64(0)
-    n = int(library().la_prefill_segments(int(n_heads), int(T), int(chunk), ctypes.byref(seg_len)))
+    n = int(library().la_prefill_segments(int(io_dtype), int(n_heads), int(T), int(chunk), ctypes.byref(seg_len)))
     return n, int(seg_len.value)
 
 

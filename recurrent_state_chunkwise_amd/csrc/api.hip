@@ -191,15 +191,19 @@ int32_t la_prefill_variant(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chu
     (void)gated;
     if (check_prefill_scalars(io_dtype, d, dv, chunk, state_dtype) != LA_OK)
         return -1;
-    return la::mfma_prefill_supported(io_dtype, d, dv, chunk) ? 1 : 0;
+    if (la::mfma_prefill_supported(io_dtype, d, dv, chunk))
+        return 1;
+    return la::mfma_f32_prefill_supported(io_dtype, d, dv, chunk) ? 2 : 0;
 }
 
-int64_t la_prefill_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t *seg_len)
+int64_t la_prefill_segments(la_dtype io_dtype, int64_t n_heads, int64_t T, int32_t chunk, int64_t *seg_len)
 {
-    if (!seg_len || n_heads < 1 || T < 1 || (chunk != 64 && chunk != 128))
+    if (!seg_len || n_heads < 1 || T < 1)
+        return -1;
+    if (!la::mfma_prefill_supported(io_dtype, 128, 128, chunk) && !la::mfma_f32_prefill_supported(io_dtype, 128, 128, chunk))
         return -1;
     int64_t nseg, len;
-    if (!la::plan_segments(n_heads, T, chunk, &nseg, &len))
+    if (!la::plan_segments(n_heads, T, chunk, 128 * dtype_bytes(io_dtype), &nseg, &len))
         return 0;
     *seg_len = len;
     return nseg;
@@ -238,6 +242,8 @@ la_status la_prefill_chunked_fm(const void *Q, const void *K, const void *V, con
     (void)hipGetLastError();
     if (la::mfma_prefill_supported(io_dtype, d, dv, chunk))
         return launched(la::launch_prefill_mfma_bf16(a, stream));
+    if (la::mfma_f32_prefill_supported(io_dtype, d, dv, chunk))
+        return launched(la::launch_prefill_mfma_f32(a, stream));
     return launched(la::launch_prefill_general(a, io_dtype, stream));
 }
 

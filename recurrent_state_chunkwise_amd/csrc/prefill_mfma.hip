@@ -38,17 +38,10 @@
 // token together with that token's denominator.
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "prefill_common.hpp"
 
 namespace la {
 namespace {
-
-typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kD = 128;          // feature width d = r and value width dv
-constexpr float kLog2e = 1.4426950408889634f;
 
 // (sequence, segment) workgroups aimed for: one per compute unit (more segments, two
 // rounds of workgroups, measured slower)
@@ -57,139 +50,6 @@ constexpr int64_t kSegmentTarget = 256;
 // per-(sequence, segment) slot in Y: S [128][128], z [128], segment gate product, pad
 constexpr int kSlotFloats = kD * kD + kD + 4;
 constexpr int64_t kMinSegTokens = (kSlotFloats * 4 + kD * 2 - 1) / (kD * 2);
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// 8 packed bf16 -> 8 floats
-__device__ __forceinline__ void unpack8(uint4 u, float *f)
-{
-    const unsigned w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-}
-
-// The feature map on the values the kernels stage as bf16 operands, where the few-ulp
-// error of the hardware exp2 and reciprocal is far below the bf16 rounding that follows.
-// ELU + 1 is the median of (x + 1, e^x, 1): x + 1 for x > 0 (where e^x > x + 1 > 1) and
-// e^x for x <= 0 (where x + 1 <= e^x <= 1).  The other maps are those of la_feature_map.
-template <int FM>
-__device__ __forceinline__ float phi(float x)
-{
-    if constexpr (FM == LA_PHI_RELU1)
-        return __builtin_fmaxf(x, 0.f) + 1.f;
-    else if constexpr (FM == LA_PHI_RELU_EPS)
-        return __builtin_fmaxf(x, 0.f) + 1e-5f;
-    else if constexpr (FM == LA_PHI_SIGMOID_EPS)
-        return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) + 1e-5f;
-    else
-        return __builtin_amdgcn_fmed3f(x + 1.f, __builtin_amdgcn_exp2f(x * kLog2e), 1.f);
-}
-
-// Buffer resources (gfx9 raw buffers): an access at or past num_records bytes reads
-// zeros and drops writes, which is how the last, partial chunk of a segment is handled.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
-// Cache policy operand of the buffer accesses: kNT marks an access non-temporal (the `nt`
-// bit), for data read for the last time or written and not read back by the library:
-// such lines are not kept in the caches, where the output rows would otherwise wait,
-// dirty, to be written back during the next kernel.
-constexpr int kNT = 2;
-template <int POL = 0>
-__device__ __forceinline__ uint4 bload16(rsrc_t r, int off)
-{
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// Gate weights inside a chunk, from lg (the in-chunk prefix sums of log alpha, zero gates
-// left out) and zp (the position of the last zero gate at or before each token, -1 if
-// none).  The weight of token i's write as token j reads it (i <= j) is the product of
-// the gates of tokens i+1..j: 0 if one of them is zero, else exp(lg_j - lg_i).  Both
-// helpers read everything they need and evaluate the exponentials unconditionally, then
-// select, so that their LDS reads are issued together rather than one behind another in
-// branches; for i > j the exponential may overflow and is discarded by the caller.
-template <bool GATED>
-__device__ __forceinline__ void pair_decays(const float *lg, const int *zp, int j, const int (&i)[4], float (&dec)[4])
-{
-    if (!GATED) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dec[r] = 1.f;
-        return;
-    }
-    const float lgj = lg[j];
-    const int zpj = zp[j];
-    float lgi[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        lgi[r] = lg[i[r]];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float e = __expf(lgj - lgi[r]);
-        dec[r] = zpj > i[r] ? 0.f : e;
-        asm volatile("" : "+v"(dec[r]));  // computed here, not sunk into the caller's i <= j branch
-    }
-}
-// write weight of token j of a chunk of n tokens: the gates after j to the chunk end;
-// 0 past the end of the chunk (where the tokens read as zeros)
-template <bool GATED>
-__device__ __forceinline__ float write_weight(const float *lg, const int *zp, int n, int j)
-{
-    float w = 1.f;
-    if (GATED) {
-        const float e = __expf(lg[n - 1] - lg[j]);
-        w = zp[n - 1] > j ? 0.f : e;
-    }
-    return j >= n ? 0.f : w;
-}
-
-// Inclusive scans over the 64 lanes of a wave with data-parallel moves (DPP): shifts by 1,
-// 2, 4 and 8 lanes inside each row of 16, then the row totals carried from lane 15 to rows
-// 1 and 3 and from lane 31 to rows 2 and 3.  A lane whose source falls outside its row, or
-// whose row is masked off, receives the identity.  Full-rate VALU moves, no LDS round trip.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ int dpp_move(int identity, int v)
-{
-    return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xf, false);
-}
-__device__ __forceinline__ float wave_scan_add(float x)
-{
-    const auto step = [](float v, int moved) { return v + __builtin_bit_cast(float, moved); };
-    const auto bits = [](float v) { return __builtin_bit_cast(int, v); };
-    x = step(x, dpp_move<0x111, 0xf>(0, bits(x)));  // row_shr:1
-    x = step(x, dpp_move<0x112, 0xf>(0, bits(x)));  // row_shr:2
-    x = step(x, dpp_move<0x114, 0xf>(0, bits(x)));  // row_shr:4
-    x = step(x, dpp_move<0x118, 0xf>(0, bits(x)));  // row_shr:8
-    x = step(x, dpp_move<0x142, 0xa>(0, bits(x)));  // row_bcast:15
-    x = step(x, dpp_move<0x143, 0xc>(0, bits(x)));  // row_bcast:31
-    return x;
-}
-__device__ __forceinline__ int wave_scan_max(int x)  // identity -1
-{
-    x = max(x, dpp_move<0x111, 0xf>(-1, x));
-    x = max(x, dpp_move<0x112, 0xf>(-1, x));
-    x = max(x, dpp_move<0x114, 0xf>(-1, x));
-    x = max(x, dpp_move<0x118, 0xf>(-1, x));
-    x = max(x, dpp_move<0x142, 0xa>(-1, x));
-    x = max(x, dpp_move<0x143, 0xc>(-1, x));
-    return x;
-}
-
-template <int C>
-struct Cfg {
-    static constexpr int NTJ = C / 16;                 // 16-token tiles per chunk
-    static constexpr int NKI = C / 32;                 // 32-token MFMA steps per chunk
-    static constexpr int NPT = NTJ * (NTJ + 1) / 2;    // tiles on or below the diagonal
-};
 
 struct Args {
     const bf16 *Q, *K, *V;
@@ -311,15 +171,6 @@ struct alignas(16) PcSmem {
     alignas(16) float gj[2][kPcC];
     alignas(16) int zp[2][kPcC];
 };
-
-// workgroup barrier with LDS visibility; reached the same number of times by every
-// wave, from the producer and the consumer loops alike
-__device__ __forceinline__ void wg_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 template <bool GATED, int FM>
 __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
@@ -1344,38 +1195,6 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
         zout[tid] = zf + (add_in ? zout[tid] : 0.f);
 }
 
-// Pass 2: entering state of every segment, in place over the segment maps.
-// slot 0 <- (S0, z0); slot p <- G_{p-1} slot(p-1) + dS_{p-1}   (p = 1 .. nseg-1)
-// The maps are read 8 at a time before the chain runs, so the loads overlap.
-__global__ __launch_bounds__(256) void segment_scan_kernel(Args a)
-{
-    const int64_t head = blockIdx.y;
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= kD * kD + kD)
-        return;
-    float run = e < kD * kD ? a.S[head * kD * kD + e] : a.z[head * kD + (e - kD * kD)];
-    slot_ptr(a, head, 0)[e] = run;
-    constexpr int kBatch = 8;
-    for (int p0 = 1; p0 < a.nseg; p0 += kBatch) {
-        float d[kBatch], g[kBatch];
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            if (p0 + q < a.nseg) {
-                const float *sl = slot_ptr(a, head, p0 + q);
-                d[q] = sl[e];
-                g[q] = sl[kD * kD + kD];
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            if (p0 + q < a.nseg) {
-                run = g[q] * run + d[q];
-                slot_ptr(a, head, p0 + q)[e] = run;
-            }
-        }
-    }
-}
-
 template <int C, bool GATED, int FM>
 hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
 {
@@ -1387,7 +1206,7 @@ hipError_t launch_c(const Args &a, int64_t n_heads, hipStream_t stream)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        segment_scan_kernel<<<dim3((kD * kD + kD + 255) / 256, (unsigned)n_heads), dim3(256), 0, stream>>>(a);
+        segment_scan_kernel<Args><<<dim3((kD * kD + kD + 255) / 256, (unsigned)n_heads), dim3(256), 0, stream>>>(a);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -1613,29 +1432,33 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // Segments per sequence: enough (sequence, segment) workgroups to give every compute
 // unit work, each segment a whole number of chunks and long enough to hold its slot in
-// Y, every segment (the last may be up to twice as long) below 2^31 bytes of Q so that
-// buffer offsets stay 32-bit.  Returns 0 when the grid would not fit.
-int64_t choose_segments(int64_t T, int64_t n_heads, int C, int64_t target)
+// Y (rows of bf16, the shorter kind), every segment (the last may be up to twice as long)
+// below 2^31 bytes of Q rows of row_bytes each so that buffer offsets stay 32-bit.
+// Returns 0 when the grid would not fit or a segment could not be kept that short.
+int64_t choose_segments(int64_t T, int64_t n_heads, int C, int64_t target, int64_t row_bytes)
 {
     int64_t nseg = (target + n_heads - 1) / n_heads;
     const int64_t min_len = ((kMinSegTokens + C - 1) / C) * C;
     if (nseg > T / min_len)
         nseg = T / min_len;
-    const int64_t max_len = ((int64_t)1 << 31) / (kD * 2) / 2;
+    const int64_t max_len = ((int64_t)1 << 31) / row_bytes / 2;
     if (nseg < (T + max_len - 1) / max_len)
         nseg = (T + max_len - 1) / max_len;
     if (nseg < 1)
         nseg = 1;
     if (n_heads * nseg > INT32_MAX)
         return 0;
+    const int64_t seg_len = nseg == 1 ? T : ((T / nseg) / C) * C;
+    if ((T - (nseg - 1) * seg_len) * row_bytes >= ((int64_t)1 << 31))
+        return 0;
     return nseg;
 }
 
 }  // namespace
 
-bool plan_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t *nseg, int64_t *seg_len)
+bool plan_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t row_bytes, int64_t *nseg, int64_t *seg_len)
 {
-    *nseg = choose_segments(T, n_heads, chunk, kSegmentTarget);
+    *nseg = choose_segments(T, n_heads, chunk, kSegmentTarget, row_bytes);
     if (*nseg == 0)
         return false;
     *seg_len = *nseg == 1 ? T : ((T / *nseg) / chunk) * chunk;  // the last segment takes the rest
@@ -1671,7 +1494,7 @@ hipError_t launch_noncausal_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
     a.eps = (float)pa.eps;
     int64_t nseg, seg_len;
     const int64_t bph = (pa.T + kNcBlockTokens - 1) / kNcBlockTokens;
-    if (!plan_segments(pa.n_heads, pa.T, kPcC, &nseg, &seg_len) || pa.n_heads * bph > INT32_MAX)
+    if (!plan_segments(pa.n_heads, pa.T, kPcC, kD * 2, &nseg, &seg_len) || pa.n_heads * bph > INT32_MAX)
         return hipErrorInvalidValue;
     a.nseg = (int)nseg;
     a.seg_len = seg_len;
@@ -1695,7 +1518,7 @@ hipError_t launch_prefill_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
 
     const int C = pa.chunk;
     int64_t nseg, seg_len;
-    if (!plan_segments(pa.n_heads, pa.T, C, &nseg, &seg_len))
+    if (!plan_segments(pa.n_heads, pa.T, C, kD * 2, &nseg, &seg_len))
         return hipErrorInvalidValue;
     a.nseg = (int)nseg;
     a.seg_len = seg_len;

@@ -133,7 +133,9 @@ def test_state_init_rejections(lib):
 def test_prefill_variant(lib):
     assert la.la_prefill_variant(BF16, 16, 16, 16, False, F32) == 0
     assert la.la_prefill_variant(F64, 16, 16, 16, False, F64) == 0
-    assert la.la_prefill_variant(F32, 128, 128, 64, True, F32) == 0
+    assert la.la_prefill_variant(F32, 128, 128, 64, True, F32) == 2   # the fp32 MFMA kernel
+    assert la.la_prefill_variant(F32, 128, 128, 128, True, F32) == 0  # fp32 at chunk 128: general
+    assert la.la_prefill_variant(F32, 64, 64, 64, False, F32) == 0
     assert la.la_prefill_variant(BF16, 128, 128, 64, False, F32) == 1
     assert la.la_prefill_variant(BF16, 128, 128, 128, True, F32) == 1
     assert la.la_prefill_variant(BF16, 128, 128, 32, True, F32) == 0
@@ -335,9 +337,27 @@ def test_segment_plan_rejections(lib):
     assert la.la_prefill_segments(0, 100, 64)[0] == -1
     assert la.la_prefill_segments(4, 0, 64)[0] == -1
     assert la.la_prefill_segments(4, 100, 32)[0] == -1
-    assert lib.la_prefill_segments(4, 100, 64, None) == -1
+    assert lib.la_prefill_segments(BF16, 4, 100, 64, None) == -1
     # the full workloads: one segment per compute unit (or per sequence past 256 sequences)
     assert la.la_prefill_segments(64, 4096, 64) == (4, 1024)
     assert la.la_prefill_segments(32, 16384, 64) == (8, 2048)
     assert la.la_prefill_segments(32, 131072, 128) == (8, 16384)
     assert la.la_prefill_segments(65536, 256, 64) == (1, 256)
+    # the fp32 kernel plans with its own 512-byte rows, at chunk 64 only
+    assert la.la_prefill_segments(64, 4096, 64, F32) == (4, 1024)
+    assert la.la_prefill_segments(64, 4096, 128, F32)[0] == -1
+    assert la.la_prefill_segments(64, 4096, 64, F64)[0] == -1
+
+
+def test_segment_plan_f32_rows(lib):
+    # fp32 rows are 512 bytes: every segment, the last included, stays below 2^31 bytes of Q
+    for T in PLAN_T:
+        for H in (1, 3, 64, 256, 65536):
+            nseg, seg_len = la.la_prefill_segments(H, T, 64, F32)
+            if nseg <= 0:
+                assert nseg == 0 and H * -(-T // ((1 << 31) // 512 // 2)) > INT32_MAX
+                continue
+            last = T - (nseg - 1) * seg_len
+            assert last * 512 < (1 << 31) and seg_len * 512 < (1 << 31), (T, H, nseg, seg_len)
+            if nseg > 1:
+                assert seg_len % 64 == 0 and seg_len * 512 >= la.la_prefill_segment_slot_bytes()
