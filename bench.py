@@ -311,6 +311,16 @@ def time_kv_state(torch, la, wl, cfg):
         la.la_prefill_chunked(hk4, hk4, hv4, None, cfg.eps, 64, Yseed, S, z)
         torch.cuda.synchronize()
         setup_peak = torch.cuda.max_memory_allocated() - base
+        # the build itself, timed over 5 more builds from a zero state (device time)
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(5):
+            la.la_state_init(S, z)
+            la.la_prefill_chunked(hk4, hk4, hv4, None, cfg.eps, 64, Yseed, S, z)
+        b1.record()
+        torch.cuda.synchronize()
+        build_ms = b0.elapsed_time(b1) / 5
         del Yseed
         S2, z2 = S.view(H, d, d), z.view(H, d)
         y = torch.empty((H, d), device="cuda", dtype=bf16)
@@ -328,6 +338,8 @@ def time_kv_state(torch, la, wl, cfg):
             "history_step_ms_graph": hist_graph_ms, "state_step_ms_graph": state_graph_ms,
             "state_over_history_time_graph": state_graph_ms / hist_graph_ms,
             "history_peak_bytes": hist_peak, "state_peak_bytes": state_peak, "state_setup_peak_bytes": setup_peak,
+            "state_build_ms": build_ms,
+            "state_build_variant": la.la_prefill_variant(la.LA_BF16, d, d, 64, False, la.LA_F32),
             "history_read_GBps_graph": hist_bytes / (hist_graph_ms / 1e3) / 1e9,
             "finite": hist_finite and state_finite,
         })

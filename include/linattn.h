@@ -125,13 +125,18 @@ la_status la_state_init(void *S, void *z, int64_t n_states, int32_t r, int32_t d
  *   z      [B, H, d]      state_dtype, same as S
  *   eps    >= 0, added to every denominator
  *   chunk  tokens per chunk, 1..128 (the last chunk of a sequence may be shorter)
- * bf16 io with d = dv = 128 and chunk 64 or 128 runs on bf16 MFMA with fp32
- * accumulation and fp32 state; every other valid request runs a general kernel
- * that computes in the state dtype.  The bf16 path splits long sequences into
- * segments and keeps each segment's state (66,064 bytes) in that segment's rows of
- * Y until they are overwritten with its outputs, so Y is working memory for the
- * duration of the call: its contents are defined only once the call's work on
- * `stream` has finished.  No other memory is used.
+ * Kernels (la_prefill_variant tells which a request takes):
+ *   - bf16 io, d = dv = 128, chunk 64 or 128: bf16 MFMA products with fp32
+ *     accumulation and fp32 state;
+ *   - chunk 64 with f32 io at d = dv = 64 or 128, or bf16 io at d = dv = 64: fp32 MFMA
+ *     products on fp32 operands (bf16 inputs widen exactly), fp32 state;
+ *   - every other valid request, and the two above when Q, K, V or Y is not aligned as
+ *     la_prefill_variant states: a general kernel that computes in the state dtype.
+ * The MFMA paths split long sequences into segments (la_prefill_segments) and keep
+ * each segment's entering state (la_prefill_segment_slot_bytes(d) bytes) in that
+ * segment's rows of Y until they are overwritten with its outputs, so Y is working
+ * memory for the duration of the call: its contents are defined only once the call's
+ * work on `stream` has finished.  No other memory is used.
  * Errors: LA_ERR_NULL, LA_ERR_SHAPE (B, H, T, d, dv < 1), LA_ERR_DTYPE, LA_ERR_EPS,
  * LA_ERR_CHUNK, LA_ERR_UNSUPPORTED (d or dv > 128, chunk > 128), LA_ERR_ALIAS,
  * LA_ERR_LAUNCH.
@@ -284,31 +289,39 @@ const char *la_status_str(la_status status);
 
 /*
  * Which prefill kernel a request would run, without running it:
- *   1 = bf16 MFMA chunked kernel (d = dv = 128, chunk 64 or 128), 2 = fp32 MFMA chunked
- *   kernel (f32 io, d = dv = 128, chunk 64), 0 = general kernel, -1 = the request is rejected
- *   (the same checks as la_prefill_chunked on the scalar arguments).
+ *   1 = bf16 MFMA chunked kernel (bf16 io, d = dv = 128, chunk 64 or 128),
+ *   2 = fp32-arithmetic MFMA chunked kernel (chunk 64: f32 io at d = dv = 64 or 128, bf16 io
+ *       at d = dv = 64),
+ *   0 = general kernel, -1 = the request is rejected (the same checks as
+ *   la_prefill_chunked on the scalar arguments).
+ * Variants 1 and 2 fall back to the general kernel at run time when Q, K, V or Y is not
+ * aligned to 16 bytes (8 bytes for bf16 io in variant 2).
  */
 int32_t la_prefill_variant(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk,
                            int32_t gated, la_dtype state_dtype);
 
 /*
- * How the MFMA prefill (d = dv = 128; bf16 io at chunk 64 or 128, f32 io at chunk 64) cuts
- * each of n_heads sequences of T tokens, without running anything: the plan
- * la_prefill_chunked uses for those requests (la_prefill_noncausal: bf16 at 64).  Sequences are cut into segments so that the
- * (sequence, segment) workgroups give every compute unit work; the state entering each
- * segment follows from the segments before it by the associative composition of gated
- * updates (section "门控递推为什么能做并行 scan").  Returns the number of segments per
- * sequence and sets *seg_len to the length of every segment but the last, which takes
- * the rest (*seg_len = T for one segment).  Every segment but the last is a whole number
- * of chunks; with more than one segment, each segment is long enough to hold, in its own
- * rows of Y, a slot of la_prefill_segment_slot_bytes() bytes where the state entering it
- * is parked before its outputs overwrite those rows, and every segment stays below 2^31
- * bytes of Q.  Returns 0 when n_heads x segments would not fit one launch (the prefill
- * then fails with LA_ERR_LAUNCH) and -1 for seg_len NULL, n_heads or T < 1, or an
- * (io_dtype, chunk) pair the MFMA prefill does not take.
+ * How the MFMA prefills (variants 1 and 2 of la_prefill_variant, at d = dv) cut each of
+ * n_heads sequences of T tokens, without running anything: the plan la_prefill_chunked
+ * uses for those requests (la_prefill_noncausal: bf16 at d = 128 and chunk 64).  Sequences
+ * are cut into segments so that the (sequence, segment) workgroups give every compute
+ * unit work; the state entering each segment follows from the segments before it by the
+ * associative composition of gated updates (section "门控递推为什么能做并行 scan").  Returns
+ * the number of segments per sequence and sets *seg_len to the length of every segment
+ * but the last, which takes the rest (*seg_len = T for one segment).  Every segment but
+ * the last is a whole number of chunks; with more than one segment, each segment is long
+ * enough to hold, in its own rows of Y, a slot of la_prefill_segment_slot_bytes(d) bytes
+ * where the state entering it is parked before its outputs overwrite those rows, and
+ * every segment stays below 2^31 bytes of Q.  Returns 0 when n_heads x segments would not
+ * fit one launch (the prefill then fails with LA_ERR_LAUNCH) and -1 for seg_len NULL,
+ * n_heads or T < 1, or an (io_dtype, d, chunk) the MFMA prefills do not take.
  */
-int64_t la_prefill_segments(la_dtype io_dtype, int64_t n_heads, int64_t T, int32_t chunk, int64_t *seg_len);
-int64_t la_prefill_segment_slot_bytes(void);
+int64_t la_prefill_segments(la_dtype io_dtype, int32_t d, int64_t n_heads, int64_t T, int32_t chunk,
+                            int64_t *seg_len);
+/* Bytes of one segment's state slot at d = dv = d (S, z and the segment's gate product in
+ * fp32, padded to 16 bytes): (d*d + d + 4) * 4; -1 for a width no MFMA prefill takes
+ * (d other than 64 or 128). */
+int64_t la_prefill_segment_slot_bytes(int32_t d);
 
 #ifdef __cplusplus
 }

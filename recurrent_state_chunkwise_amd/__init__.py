@@ -110,9 +110,9 @@ def library() -> ctypes.CDLL:
             lib.la_softmax_decode_workspace_bytes.restype = i64
             lib.la_softmax_decode_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32]
             lib.la_prefill_segments.restype = i64
-            lib.la_prefill_segments.argtypes = [ctypes.c_int, i64, i64, i32, ctypes.POINTER(i64)]
+            lib.la_prefill_segments.argtypes = [ctypes.c_int, i32, i64, i64, i32, ctypes.POINTER(i64)]
             lib.la_prefill_segment_slot_bytes.restype = i64
-            lib.la_prefill_segment_slot_bytes.argtypes = []
+            lib.la_prefill_segment_slot_bytes.argtypes = [i32]
             lib.la_prefill_variant.restype = ctypes.c_int32
             lib.la_prefill_variant.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int]
             _lib = lib
@@ -376,14 +376,16 @@ def la_prefill_variant(io_dtype: int, d: int, dv: int, chunk: int, gated: bool, 
     return int(library().la_prefill_variant(io_dtype, d, dv, chunk, int(bool(gated)), state_dtype))
 
 
-def la_prefill_segments(n_heads: int, T: int, chunk: int, io_dtype: int = LA_BF16):
-    """(segments per sequence, length of all but the last) of the MFMA prefill's plan;
-    segments = 0 when the grid would not fit a launch, -1 for invalid arguments."""
+def la_prefill_segments(n_heads: int, T: int, chunk: int, io_dtype: int = LA_BF16, d: int = 128):
+    """(segments per sequence, length of all but the last) of the MFMA prefills' plan at
+    d = dv = d; segments = 0 when the grid would not fit a launch, -1 for invalid arguments."""
     seg_len = ctypes.c_int64(0)
-    n = int(library().la_prefill_segments(int(io_dtype), int(n_heads), int(T), int(chunk), ctypes.byref(seg_len)))
+    n = int(library().la_prefill_segments(int(io_dtype), int(d), int(n_heads), int(T), int(chunk),
+                                          ctypes.byref(seg_len)))
     return n, int(seg_len.value)
 
 
-def la_prefill_segment_slot_bytes() -> int:
-    """Bytes of the state each segment after the first parks in its own rows of Y."""
-    return int(library().la_prefill_segment_slot_bytes())
+def la_prefill_segment_slot_bytes(d: int = 128) -> int:
+    """Bytes of the state each segment after the first parks in its own rows of Y (-1 for a
+    width no MFMA prefill takes)."""
+    return int(library().la_prefill_segment_slot_bytes(int(d)))

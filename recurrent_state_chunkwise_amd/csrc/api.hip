@@ -196,20 +196,24 @@ int32_t la_prefill_variant(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chu
     return la::mfma_f32_prefill_supported(io_dtype, d, dv, chunk) ? 2 : 0;
 }
 
-int64_t la_prefill_segments(la_dtype io_dtype, int64_t n_heads, int64_t T, int32_t chunk, int64_t *seg_len)
+int64_t la_prefill_segments(la_dtype io_dtype, int32_t d, int64_t n_heads, int64_t T, int32_t chunk,
+                            int64_t *seg_len)
 {
     if (!seg_len || n_heads < 1 || T < 1)
         return -1;
-    if (!la::mfma_prefill_supported(io_dtype, 128, 128, chunk) && !la::mfma_f32_prefill_supported(io_dtype, 128, 128, chunk))
+    if (!la::mfma_prefill_supported(io_dtype, d, d, chunk) && !la::mfma_f32_prefill_supported(io_dtype, d, d, chunk))
         return -1;
     int64_t nseg, len;
-    if (!la::plan_segments(n_heads, T, chunk, 128 * dtype_bytes(io_dtype), &nseg, &len))
+    if (!la::plan_segments(n_heads, T, chunk, d * dtype_bytes(io_dtype), la::segment_slot_bytes(d), &nseg, &len))
         return 0;
     *seg_len = len;
     return nseg;
 }
 
-int64_t la_prefill_segment_slot_bytes(void) { return la::segment_slot_bytes(); }
+int64_t la_prefill_segment_slot_bytes(int32_t d)
+{
+    return d == 64 || d == 128 ? la::segment_slot_bytes(d) : -1;
+}
 
 la_status la_prefill_chunked_fm(const void *Q, const void *K, const void *V, const void *alpha, la_dtype io_dtype,
                                 int64_t B, int64_t H, int64_t T, int32_t d, int32_t dv, double eps, int32_t chunk,
@@ -243,7 +247,7 @@ la_status la_prefill_chunked_fm(const void *Q, const void *K, const void *V, con
     if (la::mfma_prefill_supported(io_dtype, d, dv, chunk))
         return launched(la::launch_prefill_mfma_bf16(a, stream));
     if (la::mfma_f32_prefill_supported(io_dtype, d, dv, chunk))
-        return launched(la::launch_prefill_mfma_f32(a, stream));
+        return launched(la::launch_prefill_mfma_f32(a, io_dtype, stream));
     return launched(la::launch_prefill_general(a, io_dtype, stream));
 }
 

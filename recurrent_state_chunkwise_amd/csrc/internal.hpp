@@ -86,14 +86,17 @@ hipError_t softmax_static_workspace(void **ptr);
 
 // True when the bf16 MFMA prefill kernel handles the request.
 bool mfma_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk);
-// The MFMA prefill's cut of each sequence into segments (chunk 64 or 128; rows of row_bytes
-// bytes of Q): false when the grid would not fit a launch.
-bool plan_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t row_bytes, int64_t *nseg, int64_t *seg_len);
-// True when the fp32 MFMA prefill kernel handles the request; its launcher.
+// The MFMA prefills' cut of each sequence into segments (chunk 64 or 128; rows of row_bytes
+// bytes of Q; a state slot of slot_bytes): false when the grid would not fit a launch.
+bool plan_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t row_bytes, int64_t slot_bytes, int64_t *nseg,
+                   int64_t *seg_len);
+// True when the fp32-arithmetic MFMA prefill kernel handles the request (chunk 64; fp32
+// inputs at d = dv = 64 or 128, bf16 inputs at d = dv = 64); its launcher.
 bool mfma_f32_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk);
-hipError_t launch_prefill_mfma_f32(const PrefillArgs &a, hipStream_t stream);
-// Bytes of the state each segment after the first parks in Y at its first rows.
-int64_t segment_slot_bytes();
+hipError_t launch_prefill_mfma_f32(const PrefillArgs &a, la_dtype io_dtype, hipStream_t stream);
+// Bytes of the state (S, z, a gate product, padded) each segment after the first parks in
+// Y at its first rows, at width d = dv.
+int64_t segment_slot_bytes(int32_t d);
 bool mfma_noncausal_supported(la_dtype io_dtype, int32_t d, int32_t dv);
 
 }  // namespace la

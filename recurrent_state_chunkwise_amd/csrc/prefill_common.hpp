@@ -161,15 +161,16 @@ __device__ __forceinline__ void wg_barrier()
 // Pass 2: entering state of every segment, in place over the segment maps.
 // slot 0 <- (S0, z0); slot p <- G_{p-1} slot(p-1) + dS_{p-1}   (p = 1 .. nseg-1)
 // The maps are read 8 at a time before the chain runs, so the loads overlap.
-// A is the argument block of the pass (bf16 or fp32 inputs); slot_ptr(a, head, p) locates slot p.
-template <typename A>
+// A is the argument block of the pass; slot_ptr(a, head, p) locates slot p: S [D][D], z [D],
+// then the segment's gate product.
+template <typename A, int D = kD>
 __global__ __launch_bounds__(256) void segment_scan_kernel(A a)
 {
     const int64_t head = blockIdx.y;
     const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= kD * kD + kD)
+    if (e >= D * D + D)
         return;
-    float run = e < kD * kD ? a.S[head * kD * kD + e] : a.z[head * kD + (e - kD * kD)];
+    float run = e < D * D ? a.S[head * D * D + e] : a.z[head * D + (e - D * D)];
     slot_ptr(a, head, 0)[e] = run;
     constexpr int kBatch = 8;
     for (int p0 = 1; p0 < a.nseg; p0 += kBatch) {
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(A a)
             if (p0 + q < a.nseg) {
                 const float *sl = slot_ptr(a, head, p0 + q);
                 d[q] = sl[e];
-                g[q] = sl[kD * kD + kD];
+                g[q] = sl[D * D + D];
             }
         }
 #pragma unroll

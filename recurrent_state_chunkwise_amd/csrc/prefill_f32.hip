@@ -1,4 +1,5 @@
-// fp32-input MFMA chunked prefill for d = dv = 128 at chunk 64, fp32 state.
+// fp32-arithmetic MFMA chunked prefill at chunk 64, fp32 state: d = dv = 128 with fp32
+// inputs, and d = dv = 64 with fp32 or bf16 inputs (bf16 values widen to fp32 exactly).
 //
 // The chunk equations of the page "Linear attention：把历史写进状态" (hs-black.github.io),
 // section "一个 chunk 的输出由两部分组成", with the gate products of section "加一个门" folded
@@ -9,7 +10,7 @@
 // entering state, writing y and, for the last segment, the final S and z.
 //
 // Every product is v_mfma_f32_16x16x4_f32 on fp32 operands with fp32 accumulation, so
-// nothing is rounded below fp32 (the fp32 bar is 1e-4).  Lane (lr, g) of a 16x16x4 product
+// nothing is rounded below fp32 before y is stored.  Lane (lr, g) of a 16x16x4 product
 // supplies A[lr][g] and B[g][lr]; lane (lr, g) of its 16x16 result holds rows 4g .. 4g+3
 // of column lr.  The contraction order is permuted so that the operands come straight out
 // of registers or one 16-byte LDS read serves four products:
@@ -19,17 +20,20 @@
 //   (3) N^T += V^T P^T: K step (ti, r) takes tokens 16ti + 4g + r, whose score values are
 //       register r of the score tile's accumulator lane (lr, g), kept in LDS in that layout;
 //   (4) S += (w K~)^T V: K step (u, r) takes tokens 16u + 4g + r.
-// Q~ and K~ are staged token-major (rows of 128 floats), V and the write weights
+// Q~ and K~ are staged token-major (rows of D floats), V and the write weights
 // feature-major (rows of 64 tokens), each row padded by 4 floats, so that every operand
 // is a float4 per lane and each 16-lane group reads 64 distinct banks.
 //
-// One workgroup of 8 waves per (sequence, segment); wave w owns value columns 16w .. 16w+15
-// of S and of the outputs.  Per chunk all waves first stage the chunk (feature map, write
-// weights, transposes) from the registers into which its raw rows were loaded during the
-// previous chunk's products, then do the products; the products take several times the
-// memory time of a chunk, so the loads have that long to arrive.  The row sums of the
-// masked scores (the intra-chunk denominator) are formed in fp32 from the scores, z from
-// the fp32 write weights.
+// One workgroup of D/16 waves per (sequence, segment); wave w owns value columns
+// 16w .. 16w+15 of S and of the outputs.  Per chunk all waves first stage the chunk
+// (feature map, write weights, transposes) from the registers into which its raw rows were
+// loaded during the previous chunk's products, then do the products; the products take
+// several times the memory time of a chunk, so the loads have that long to arrive.  The row
+// sums of the masked scores (the intra-chunk denominator) are formed in fp32 from the
+// scores, z from the fp32 write weights.  At D = 64 the tiles take under 80 KB of LDS, so
+// two workgroups share a compute unit.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 #include "prefill_common.hpp"
@@ -37,22 +41,29 @@
 namespace la {
 namespace {
 
-constexpr int kFC = 64;           // chunk
-constexpr int kFWaves = 8;
-constexpr int kFThreads = 64 * kFWaves;
-constexpr int kQRow = kD + 4;     // row of the token-major tiles, in floats (528 bytes)
-constexpr int kTRow = kFC + 4;    // row of the feature-major tiles, in floats (272 bytes)
-constexpr int kFTiles = 10;       // 16x16 score tiles on or below the diagonal of a chunk
+constexpr int kFC = 64;      // chunk
+constexpr int kTRow = kFC + 4;  // row of the feature-major tiles, in floats (272 bytes)
+constexpr int kFTiles = 10;  // 16x16 score tiles on or below the diagonal of a chunk
+
+template <int D>
+struct FShape {
+    static_assert(D == 64 || D == 128, "the fp32-arithmetic prefill takes d = dv = 64 or 128");
+    static constexpr int tiles = D / 16;    // 16-wide feature or value tiles, = waves
+    static constexpr int threads = 64 * tiles;
+    static constexpr int quads = D / 4;     // 4-feature pieces of a row
+    static constexpr int qrow = D + 4;      // row of the token-major tiles, in floats
+};
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+template <typename TI, int D>
 struct FArgs {
-    const float *Q, *K, *V;
+    const TI *Q, *K, *V;
     const float *alpha;
-    float *Y;
+    TI *Y;
     float *S, *z;
     int64_t T;
     int64_t seg_len;
@@ -60,26 +71,36 @@ struct FArgs {
     float eps;
 };
 
-// slot p of a sequence: S, z and the segment's gate product, parked in the first rows of
-// segment p of Y
-__device__ __forceinline__ float *slot_ptr(const FArgs &a, int64_t head, int p)
+// slot p of a sequence: S [D][D], z [D] and the segment's gate product, parked in the first
+// rows of segment p of Y
+template <typename TI, int D>
+__device__ __forceinline__ float *slot_ptr(const FArgs<TI, D> &a, int64_t head, int p)
 {
-    return a.Y + (head * a.T + (int64_t)p * a.seg_len) * kD;
+    return reinterpret_cast<float *>(a.Y + (head * a.T + (int64_t)p * a.seg_len) * D);
 }
 
 // Raw rows of one chunk held in registers between their load and their staging: thread
-// (fq, tq) holds features 4fq .. 4fq+3 of tokens 4tq .. 4tq+3 (fq = tid & 31, tq = tid >> 5),
-// so that the feature-major tiles are written as float4 runs of 4 tokens.
+// (fq, tq) holds features 4fq .. 4fq+3 of tokens 4tq .. 4tq+3 (fq = tid mod D/4,
+// tq = tid div D/4, 0 .. 15), so that the feature-major tiles are written as float4 runs of
+// 4 tokens.
 struct Quad {
     f32x4 x[4];  // x[s] = the 4 features of token 4tq + s
 };
 
+template <typename TI, int D>
 __device__ __forceinline__ void load_quad(rsrc_t r, int c, int fq, int tq, Quad &q)
 {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const uint4 u = bload16(r, ((c * kFC + 4 * tq + s) * kD + 4 * fq) * 4);
-        q.x[s] = f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+        const int e = (c * kFC + 4 * tq + s) * D + 4 * fq;  // element offset in the segment
+        if constexpr (std::is_same_v<TI, float>) {
+            const uint4 u = bload16(r, e * 4);
+            q.x[s] = f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+        } else {
+            const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, e * 2, 0, 0);
+            q.x[s] = f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                           __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
+        }
     }
 }
 
@@ -104,12 +125,12 @@ __device__ __forceinline__ void scan_gates(float av_raw, int n, int lane, float 
     gj[lane] = zf >= 0 ? 0.f : __expf(s);
 }
 
-// Write weights of one token quad and the raw K rows: w phi(k) feature-major into KwT, and
-// the fp32 sums over the 4 tokens for z into zred.  Tokens past the end of the segment (whose
-// K rows load as zeros) weigh 0.
-template <bool GATED, int FM>
+// Write weights of one token quad: w phi(k) feature-major into KwT, and phi(k) token-major
+// into Ks when given.  Tokens past the end of the segment (whose K rows load as zeros)
+// weigh 0.
+template <int D, bool GATED, int FM>
 __device__ __forceinline__ void stage_weights(const Quad &rk, const float *lg, const int *zp, int n, int fq,
-                                              int tq, float *KwT, float *zred_row, float *Ks)
+                                              int tq, float *KwT, float *Ks)
 {
     f32x4 f[4];
     float w[4];
@@ -118,16 +139,12 @@ __device__ __forceinline__ void stage_weights(const Quad &rk, const float *lg, c
         f[s] = phi4<FM>(rk.x[s]);
         w[s] = write_weight<GATED>(lg, zp, n, 4 * tq + s);
         if (Ks)
-            *reinterpret_cast<f32x4 *>(&Ks[(4 * tq + s) * kQRow + 4 * fq]) = f[s];
+            *reinterpret_cast<f32x4 *>(&Ks[(4 * tq + s) * FShape<D>::qrow + 4 * fq]) = f[s];
     }
-    f32x4 zq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const f32x4 col = {w[0] * f[0][e], w[1] * f[1][e], w[2] * f[2][e], w[3] * f[3][e]};
-        *reinterpret_cast<f32x4 *>(&KwT[(4 * fq + e) * kTRow + 4 * tq]) = col;
-        zq[e] = (col[0] + col[1]) + (col[2] + col[3]);
-    }
-    *reinterpret_cast<f32x4 *>(&zred_row[4 * fq]) = zq;
+    for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<f32x4 *>(&KwT[(4 * fq + e) * kTRow + 4 * tq]) =
+            f32x4{w[0] * f[0][e], w[1] * f[1][e], w[2] * f[2][e], w[3] * f[3][e]};
 }
 
 // V rows of one token quad, feature-major into VT
@@ -139,16 +156,30 @@ __device__ __forceinline__ void stage_values(const Quad &rv, int fq, int tq, flo
             f32x4{rv.x[0][e], rv.x[1][e], rv.x[2][e], rv.x[3][e]};
 }
 
+// The chunk's write to z of feature f: the sum of row f of KwT, by token quads in order
+// (each quad summed pairwise)
+__device__ __forceinline__ float chunk_dz(const float *KwT, int f)
+{
+    float dz = 0.f;
+#pragma unroll
+    for (int u = 0; u < kFC / 4; ++u) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(&KwT[f * kTRow + 4 * u]);
+        dz += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+    return dz;
+}
+
 // (4) of wave w: S[16tf + 4g + r][16w + lr] (sacc[tf][r] of lane (lr, g)) += sum over the 64
 // tokens i of w_i phi(k_i)[f] v_i[c], with K step (u, r) taking tokens 16u + 4g + r
-__device__ __forceinline__ void state_write(f32x4 (&sacc)[8], const float *KwT, const float *VT, int wave, int lr,
-                                            int g)
+template <int D>
+__device__ __forceinline__ void state_write(f32x4 (&sacc)[D / 16], const float *KwT, const float *VT, int wave,
+                                            int lr, int g)
 {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const f32x4 vb = *reinterpret_cast<const f32x4 *>(&VT[(16 * wave + lr) * kTRow + 16 * u + 4 * g]);
 #pragma unroll
-        for (int tf = 0; tf < 8; ++tf) {
+        for (int tf = 0; tf < D / 16; ++tf) {
             const f32x4 ka = *reinterpret_cast<const f32x4 *>(&KwT[(16 * tf + lr) * kTRow + 16 * u + 4 * g]);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -158,10 +189,10 @@ __device__ __forceinline__ void state_write(f32x4 (&sacc)[8], const float *KwT, 
 }
 
 // ============================================================================ pass 1
+template <int D>
 struct alignas(16) F32SumSmem {
-    alignas(16) float VT[kD * kTRow];
-    alignas(16) float KwT[kD * kTRow];
-    alignas(16) float zred[16][kD];  // z update of the chunk per token quad
+    alignas(16) float VT[D * kTRow];
+    alignas(16) float KwT[D * kTRow];
     alignas(16) float lg[2][kFC];
     alignas(16) float gj[2][kFC];
     alignas(16) int zp[2][kFC];
@@ -170,15 +201,16 @@ struct alignas(16) F32SumSmem {
 // Segment map of every non-final segment (from a zero state): S and z, then the product of
 // the segment's gates, into the next segment's slot.  Segment-major block order spreads the
 // idle last-segment workgroups over the XCDs.
-template <bool GATED, int FM>
-__global__ __launch_bounds__(kFThreads) void summary_f32_kernel(FArgs a)
+template <typename TI, int D, bool GATED, int FM>
+__global__ __launch_bounds__(FShape<D>::threads) void summary_f32_kernel(FArgs<TI, D> a)
 {
-    __shared__ F32SumSmem sm;
+    using Sh = FShape<D>;
+    __shared__ F32SumSmem<D> sm;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int lr = lane & 15, g = lane >> 4;
-    const int fq = tid & 31, tq = tid >> 5;
+    const int fq = tid % Sh::quads, tq = tid / Sh::quads;
 
     const int64_t n_heads = gridDim.x / a.nseg;
     const int64_t head = blockIdx.x % n_heads;
@@ -190,19 +222,20 @@ __global__ __launch_bounds__(kFThreads) void summary_f32_kernel(FArgs a)
     const int n_chunks = (int)((len + kFC - 1) / kFC);
     auto chunk_len = [&](int c) { return (int)min((int64_t)kFC, len - (int64_t)c * kFC); };
     const int64_t row0 = head * a.T + s0;
-    const rsrc_t rK = make_rsrc(a.K + row0 * kD, len * kD * 4);
-    const rsrc_t rV = make_rsrc(a.V + row0 * kD, len * kD * 4);
+    const int64_t seg_bytes = len * D * (int64_t)sizeof(TI);
+    const rsrc_t rK = make_rsrc(a.K + row0 * D, seg_bytes);
+    const rsrc_t rV = make_rsrc(a.V + row0 * D, seg_bytes);
     const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
 
-    f32x4 sacc[8];
+    f32x4 sacc[Sh::tiles];
 #pragma unroll
-    for (int tf = 0; tf < 8; ++tf)
+    for (int tf = 0; tf < Sh::tiles; ++tf)
         sacc[tf] = f32x4{0.f, 0.f, 0.f, 0.f};
     float zreg = 0.f, g_seg = 1.f;
     Quad rk, rv;
     float ar = 0.f;
-    load_quad(rK, 0, fq, tq, rk);
-    load_quad(rV, 0, fq, tq, rv);
+    load_quad<TI, D>(rK, 0, fq, tq, rk);
+    load_quad<TI, D>(rV, 0, fq, tq, rv);
     if (GATED && wave == 0)
         ar = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, lane * 4, 0, 0));
 
@@ -212,10 +245,10 @@ __global__ __launch_bounds__(kFThreads) void summary_f32_kernel(FArgs a)
         if (GATED && wave == 0)
             scan_gates(ar, n, lane, sm.lg[gs], sm.zp[gs], sm.gj[gs]);
         wg_barrier();  // gates visible; the previous chunk's products are done with the tiles
-        stage_weights<GATED, FM>(rk, sm.lg[gs], sm.zp[gs], n, fq, tq, sm.KwT, sm.zred[tq], nullptr);
+        stage_weights<D, GATED, FM>(rk, sm.lg[gs], sm.zp[gs], n, fq, tq, sm.KwT, nullptr);
         stage_values(rv, fq, tq, sm.VT);
-        load_quad(rK, c + 1, fq, tq, rk);  // past the end of the segment these read zeros
-        load_quad(rV, c + 1, fq, tq, rv);
+        load_quad<TI, D>(rK, c + 1, fq, tq, rk);  // past the end of the segment these read zeros
+        load_quad<TI, D>(rV, c + 1, fq, tq, rv);
         if (GATED && wave == 0)
             ar = __uint_as_float(
                 (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, ((c + 1) * kFC + lane) * 4, 0, 0));
@@ -224,57 +257,58 @@ __global__ __launch_bounds__(kFThreads) void summary_f32_kernel(FArgs a)
         if (GATED) {
             g_seg *= g_end;
 #pragma unroll
-            for (int tf = 0; tf < 8; ++tf)
+            for (int tf = 0; tf < Sh::tiles; ++tf)
                 sacc[tf] *= g_end;
         }
-        state_write(sacc, sm.KwT, sm.VT, wave, lr, g);
-        if (tid < kD) {
-            float dz = 0.f;
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                dz += sm.zred[t][tid];
-            zreg = g_end * zreg + dz;
-        }
+        state_write<D>(sacc, sm.KwT, sm.VT, wave, lr, g);
+        if (tid < D)
+            zreg = g_end * zreg + chunk_dz(sm.KwT, tid);
     }
 
     float *Sout = slot_ptr(a, head, seg + 1);
     if (tid == 0)
-        Sout[kD * kD + kD] = g_seg;
+        Sout[D * D + D] = g_seg;
 #pragma unroll
-    for (int tf = 0; tf < 8; ++tf)
+    for (int tf = 0; tf < Sh::tiles; ++tf)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            Sout[(16 * tf + 4 * g + r) * kD + 16 * wave + lr] = sacc[tf][r];
-    if (tid < kD)
-        Sout[kD * kD + tid] = zreg;
+            Sout[(16 * tf + 4 * g + r) * D + 16 * wave + lr] = sacc[tf][r];
+    if (tid < D)
+        Sout[D * D + tid] = zreg;
 }
 
 // ============================================================================ pass 3
+// The gates need one buffer: they are rewritten (by wave 0, at the top of the next chunk)
+// only after every wave has passed the barrier between the products, and what the second
+// half of the products needs of them is read into registers before it.
+template <int D>
 struct alignas(16) F32Smem {
-    alignas(16) float Qs[kFC * kQRow];  // phi(q), token-major
-    alignas(16) float Ks[kFC * kQRow];  // phi(k), token-major
-    alignas(16) float VT[kD * kTRow];   // v, feature-major
-    alignas(16) float KwT[kD * kTRow];  // w phi(k), feature-major; 0 past the end of the segment
-    alignas(16) f32x4 P[kFTiles * 64];  // masked, gate-weighted scores, accumulator layout
-    alignas(16) float rs[4][kFC];       // rs[ti][j]: row sum of score tile (tile of j, ti)
-    alignas(16) float zs[2][kD];        // z entering the chunk, by chunk parity
-    alignas(16) float zred[16][kD];
-    alignas(16) float dq[kFC];          // phi(q_j) . z_prev
-    alignas(16) float lg[2][kFC];
-    alignas(16) float gj[2][kFC];
-    alignas(16) int zp[2][kFC];
+    alignas(16) float Qs[kFC * FShape<D>::qrow];  // phi(q), token-major
+    alignas(16) float Ks[kFC * FShape<D>::qrow];  // phi(k), token-major
+    alignas(16) float VT[D * kTRow];              // v, feature-major
+    alignas(16) float KwT[D * kTRow];             // w phi(k), feature-major; 0 past the end of the segment
+    alignas(16) f32x4 P[kFTiles * 64];            // masked, gate-weighted scores, accumulator layout
+    alignas(16) float rs[kFTiles * 16];           // rs[16k + lr]: score tile k's sum over its 16 tokens i
+    alignas(16) float zs[D];                      // z entering the chunk
+    alignas(16) float dq[kFC];                    // phi(q_j) . z_prev
+    alignas(16) float lg[kFC];
+    alignas(16) float gj[kFC];
+    alignas(16) int zp[kFC];
 };
-static_assert(sizeof(F32Smem) <= 160 * 1024, "the fp32 tiles must fit in the 160 KB of LDS");
+static_assert(sizeof(F32Smem<128>) <= 160 * 1024, "the fp32 tiles must fit in the 160 KB of LDS");
+static_assert(sizeof(F32Smem<64>) <= 80 * 1024, "two workgroups of the d = 64 tiles must share the LDS");
 
-template <bool GATED, int FM>
-__global__ __launch_bounds__(kFThreads) void prefill_f32_kernel(FArgs a)
+template <typename TI, int D, bool GATED, int FM>
+__global__ __launch_bounds__(FShape<D>::threads) void prefill_f32_kernel(FArgs<TI, D> a)
 {
-    __shared__ F32Smem sm;
+    using Sh = FShape<D>;
+    constexpr int QR = Sh::qrow;
+    __shared__ F32Smem<D> sm;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int lr = lane & 15, g = lane >> 4;
-    const int fq = tid & 31, tq = tid >> 5;
+    const int fq = tid % Sh::quads, tq = tid / Sh::quads;
 
     const int64_t head = blockIdx.x / a.nseg;
     const int seg = blockIdx.x % a.nseg;
@@ -284,67 +318,74 @@ __global__ __launch_bounds__(kFThreads) void prefill_f32_kernel(FArgs a)
     const int n_chunks = (int)((len + kFC - 1) / kFC);
     auto chunk_len = [&](int c) { return (int)min((int64_t)kFC, len - (int64_t)c * kFC); };
     const int64_t row0 = head * a.T + s0;
-    const rsrc_t rQ = make_rsrc(a.Q + row0 * kD, len * kD * 4);
-    const rsrc_t rK = make_rsrc(a.K + row0 * kD, len * kD * 4);
-    const rsrc_t rV = make_rsrc(a.V + row0 * kD, len * kD * 4);
+    const int64_t seg_bytes = len * D * (int64_t)sizeof(TI);
+    const rsrc_t rQ = make_rsrc(a.Q + row0 * D, seg_bytes);
+    const rsrc_t rK = make_rsrc(a.K + row0 * D, seg_bytes);
+    const rsrc_t rV = make_rsrc(a.V + row0 * D, seg_bytes);
     const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
-    const rsrc_t rY = make_rsrc(a.Y + row0 * kD, len * kD * 4);
+    const rsrc_t rY = make_rsrc(a.Y + row0 * D, seg_bytes);
 
     // wave w owns columns 16w + lr of S: sacc[tf][r] = S[16tf + 4g + r][16w + lr]
-    f32x4 sacc[8];
-    float zreg = 0.f;  // threads tid < 128: z of feature tid
+    f32x4 sacc[Sh::tiles];
+    float zreg = 0.f;  // threads tid < D: z of feature tid
     {
-        const float *Sin = a.nseg == 1 ? a.S + head * kD * kD : slot_ptr(a, head, seg);
-        const float *zin = a.nseg == 1 ? a.z + head * kD : Sin + kD * kD;
+        const float *Sin = a.nseg == 1 ? a.S + head * D * D : slot_ptr(a, head, seg);
+        const float *zin = a.nseg == 1 ? a.z + head * D : Sin + D * D;
 #pragma unroll
-        for (int tf = 0; tf < 8; ++tf)
+        for (int tf = 0; tf < Sh::tiles; ++tf)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                sacc[tf][r] = Sin[(16 * tf + 4 * g + r) * kD + 16 * wave + lr];
-        if (tid < kD) {
+                sacc[tf][r] = Sin[(16 * tf + 4 * g + r) * D + 16 * wave + lr];
+        if (tid < D) {
             zreg = zin[tid];
-            sm.zs[0][tid] = zreg;
+            sm.zs[tid] = zreg;
         }
     }
     Quad rq, rk, rv;
     float ar = 0.f;
-    load_quad(rQ, 0, fq, tq, rq);
-    load_quad(rK, 0, fq, tq, rk);
-    load_quad(rV, 0, fq, tq, rv);
+    load_quad<TI, D>(rQ, 0, fq, tq, rq);
+    load_quad<TI, D>(rK, 0, fq, tq, rk);
+    load_quad<TI, D>(rV, 0, fq, tq, rv);
     if (GATED && wave == 0)
         ar = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, lane * 4, 0, 0));
 
     for (int c = 0; c < n_chunks; ++c) {
-        const int buf = c & 1;
         const int n = chunk_len(c);
         if (GATED && wave == 0)
-            scan_gates(ar, n, lane, sm.lg[buf], sm.zp[buf], sm.gj[buf]);
+            scan_gates(ar, n, lane, sm.lg, sm.zp, sm.gj);
         wg_barrier();  // gates visible; the previous chunk's products are done with the tiles
         // ---- staging: phi(q) and phi(k) token-major, the write weights and V feature-major
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            *reinterpret_cast<f32x4 *>(&sm.Qs[(4 * tq + s) * kQRow + 4 * fq]) = phi4<FM>(rq.x[s]);
-        stage_weights<GATED, FM>(rk, sm.lg[buf], sm.zp[buf], n, fq, tq, sm.KwT, sm.zred[tq], sm.Ks);
+            *reinterpret_cast<f32x4 *>(&sm.Qs[(4 * tq + s) * QR + 4 * fq]) = phi4<FM>(rq.x[s]);
+        stage_weights<D, GATED, FM>(rk, sm.lg, sm.zp, n, fq, tq, sm.KwT, sm.Ks);
         stage_values(rv, fq, tq, sm.VT);
-        load_quad(rQ, c + 1, fq, tq, rq);  // past the end of the segment these read zeros
-        load_quad(rK, c + 1, fq, tq, rk);
-        load_quad(rV, c + 1, fq, tq, rv);
+        load_quad<TI, D>(rQ, c + 1, fq, tq, rq);  // past the end of the segment these read zeros
+        load_quad<TI, D>(rK, c + 1, fq, tq, rk);
+        load_quad<TI, D>(rV, c + 1, fq, tq, rv);
         if (GATED && wave == 0)
             ar = __uint_as_float(
                 (unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, ((c + 1) * kFC + lane) * 4, 0, 0));
         wg_barrier();  // chunk staged
 
         // ---- part a: (2) for the four token tiles; phi(q) . z_prev (waves 0-3, token tile
-        //      `wave`); score tiles `wave` and `wave` + 8 with their row sums
+        //      `wave`); the score tiles k = wave (mod waves) with their row sums
+        float gjr[4], g_end = 1.f;  // gate products the part b below needs
+        if (GATED) {
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj)
+                gjr[tj] = sm.gj[16 * tj + lr];
+            g_end = sm.gj[n - 1];
+        }
         f32x4 acc[4];
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj)
             acc[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tf = 0; tf < 8; ++tf) {
+        for (int tf = 0; tf < Sh::tiles; ++tf) {
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj) {
-                const f32x4 qv = *reinterpret_cast<const f32x4 *>(&sm.Qs[(16 * tj + lr) * kQRow + 16 * tf + 4 * g]);
+                const f32x4 qv = *reinterpret_cast<const f32x4 *>(&sm.Qs[(16 * tj + lr) * QR + 16 * tf + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc[tj] = mfma4(sacc[tf][r], qv[r], acc[tj]);
@@ -353,10 +394,9 @@ __global__ __launch_bounds__(kFThreads) void prefill_f32_kernel(FArgs a)
         if (wave < 4) {
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int tf = 0; tf < 8; ++tf) {
-                const f32x4 zv = *reinterpret_cast<const f32x4 *>(&sm.zs[buf][16 * tf + 4 * g]);
-                const f32x4 qv =
-                    *reinterpret_cast<const f32x4 *>(&sm.Qs[(16 * wave + lr) * kQRow + 16 * tf + 4 * g]);
+            for (int tf = 0; tf < Sh::tiles; ++tf) {
+                const f32x4 zv = *reinterpret_cast<const f32x4 *>(&sm.zs[16 * tf + 4 * g]);
+                const f32x4 qv = *reinterpret_cast<const f32x4 *>(&sm.Qs[(16 * wave + lr) * QR + 16 * tf + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     d = mfma4(zv[r], qv[r], d);
@@ -364,16 +404,16 @@ __global__ __launch_bounds__(kFThreads) void prefill_f32_kernel(FArgs a)
             if (g == 0)
                 sm.dq[16 * wave + lr] = d[0];
         }
-        for (int k = wave; k < kFTiles; k += kFWaves) {
+        for (int k = wave; k < kFTiles; k += Sh::tiles) {
             const int tj = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
             const int ti = k - tj * (tj + 1) / 2;
             // sc[r] = score (i = 16ti + 4g + r, j = 16tj + lr)
             const int j = 16 * tj + lr;
             f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const f32x4 ka = *reinterpret_cast<const f32x4 *>(&sm.Ks[(16 * ti + lr) * kQRow + 16 * t + 4 * g]);
-                const f32x4 qb = *reinterpret_cast<const f32x4 *>(&sm.Qs[j * kQRow + 16 * t + 4 * g]);
+            for (int t = 0; t < Sh::tiles; ++t) {
+                const f32x4 ka = *reinterpret_cast<const f32x4 *>(&sm.Ks[(16 * ti + lr) * QR + 16 * t + 4 * g]);
+                const f32x4 qb = *reinterpret_cast<const f32x4 *>(&sm.Qs[j * QR + 16 * t + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sc = mfma4(ka[r], qb[r], sc);
@@ -383,7 +423,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_f32_kernel(FArgs a)
             for (int r = 0; r < 4; ++r)
                 ii[r] = 16 * ti + 4 * g + r;
             float dec[4];
-            pair_decays<GATED>(sm.lg[buf], sm.zp[buf], j, ii, dec);
+            pair_decays<GATED>(sm.lg, sm.zp, j, ii, dec);
             f32x4 p;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -394,7 +434,7 @@ __global__ __launch_bounds__(kFThreads) void prefill_f32_kernel(FArgs a)
             rsum += __shfl_xor(rsum, 16, 64);
             rsum += __shfl_xor(rsum, 32, 64);
             if (g == 0)
-                sm.rs[ti][j] = rsum;
+                sm.rs[16 * k + lr] = rsum;
         }
         wg_barrier();  // a | b
 
@@ -404,14 +444,14 @@ __global__ __launch_bounds__(kFThreads) void prefill_f32_kernel(FArgs a)
             const int j = 16 * tj + lr;
             float den = sm.dq[j];
             if (GATED) {
-                const float gjj = sm.gj[buf][j];
-                acc[tj] *= gjj;
-                den *= gjj;
+                acc[tj] *= gjr[tj];
+                den *= gjr[tj];
             }
 #pragma unroll
             for (int ti = 0; ti <= tj; ++ti) {
-                den += sm.rs[ti][j];
-                const f32x4 pv = sm.P[(tj * (tj + 1) / 2 + ti) * 64 + lane];
+                const int k = tj * (tj + 1) / 2 + ti;
+                den += sm.rs[16 * k + lr];
+                const f32x4 pv = sm.P[k * 64 + lane];
                 const f32x4 va = *reinterpret_cast<const f32x4 *>(&sm.VT[(16 * wave + lr) * kTRow + 16 * ti + 4 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -420,88 +460,106 @@ __global__ __launch_bounds__(kFThreads) void prefill_f32_kernel(FArgs a)
             const float inv = 1.f / (den + a.eps);
             const f32x4 y = acc[tj] * inv;
             // columns 16w + 4g .. + 3 of token j; rows past the end fall outside rY
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, y),
-                                                   rY, ((c * kFC + j) * kD + 16 * wave + 4 * g) * 4, 0, 0);
+            const int e = (c * kFC + j) * D + 16 * wave + 4 * g;
+            if constexpr (std::is_same_v<TI, float>) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, y),
+                                                       rY, e * 4, 0, 0);
+            } else {
+                const bf16x4 yb = {static_cast<bf16>(y[0]), static_cast<bf16>(y[1]), static_cast<bf16>(y[2]),
+                                   static_cast<bf16>(y[3])};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, yb),
+                                                      rY, e * 2, 0, 0);
+            }
         }
-        const float g_end = GATED ? sm.gj[buf][n - 1] : 1.f;
         if (GATED) {
 #pragma unroll
-            for (int tf = 0; tf < 8; ++tf)
+            for (int tf = 0; tf < Sh::tiles; ++tf)
                 sacc[tf] *= g_end;
         }
-        state_write(sacc, sm.KwT, sm.VT, wave, lr, g);
-        if (tid < kD) {
-            float dz = 0.f;
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                dz += sm.zred[t][tid];
-            zreg = g_end * zreg + dz;
-            sm.zs[buf ^ 1][tid] = zreg;
+        state_write<D>(sacc, sm.KwT, sm.VT, wave, lr, g);
+        if (tid < D) {
+            zreg = g_end * zreg + chunk_dz(sm.KwT, tid);
+            sm.zs[tid] = zreg;  // read again only after the next chunk's two barriers
         }
     }
 
     if (seg != a.nseg - 1)
         return;
-    float *Sout = a.S + head * kD * kD;
+    float *Sout = a.S + head * D * D;
 #pragma unroll
-    for (int tf = 0; tf < 8; ++tf)
+    for (int tf = 0; tf < Sh::tiles; ++tf)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            Sout[(16 * tf + 4 * g + r) * kD + 16 * wave + lr] = sacc[tf][r];
-    if (tid < kD)
-        a.z[head * kD + tid] = zreg;
+            Sout[(16 * tf + 4 * g + r) * D + 16 * wave + lr] = sacc[tf][r];
+    if (tid < D)
+        a.z[head * D + tid] = zreg;
 }
 
-template <bool GATED, int FM>
-hipError_t launch_f32(const FArgs &a, int64_t n_heads, hipStream_t stream)
+template <typename TI, int D, bool GATED, int FM>
+hipError_t launch_f32(const FArgs<TI, D> &a, int64_t n_heads, hipStream_t stream)
 {
+    constexpr int NT = FShape<D>::threads;
     const unsigned blocks = (unsigned)(n_heads * a.nseg);
     if (a.nseg > 1) {
-        summary_f32_kernel<GATED, FM><<<dim3(blocks), dim3(kFThreads), 0, stream>>>(a);
+        summary_f32_kernel<TI, D, GATED, FM><<<dim3(blocks), dim3(NT), 0, stream>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        segment_scan_kernel<FArgs><<<dim3((kD * kD + kD + 255) / 256, (unsigned)n_heads), dim3(256), 0, stream>>>(a);
+        segment_scan_kernel<FArgs<TI, D>, D>
+            <<<dim3((D * D + D + 255) / 256, (unsigned)n_heads), dim3(256), 0, stream>>>(a);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    prefill_f32_kernel<GATED, FM><<<dim3(blocks), dim3(kFThreads), 0, stream>>>(a);
+    prefill_f32_kernel<TI, D, GATED, FM><<<dim3(blocks), dim3(NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-
-}  // namespace
-
-bool mfma_f32_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk)
+template <typename TI, int D>
+hipError_t launch_typed(const PrefillArgs &pa, hipStream_t stream)
 {
-    return io_dtype == LA_F32 && d == kD && dv == kD && chunk == kFC;
-}
-
-hipError_t launch_prefill_mfma_f32(const PrefillArgs &pa, hipStream_t stream)
-{
-    if (!aligned16(pa.Q) || !aligned16(pa.K) || !aligned16(pa.V) || !aligned16(pa.Y))
-        return launch_prefill_general(pa, LA_F32, stream);
-    FArgs a;
-    a.Q = static_cast<const float *>(pa.Q);
-    a.K = static_cast<const float *>(pa.K);
-    a.V = static_cast<const float *>(pa.V);
+    FArgs<TI, D> a;
+    a.Q = static_cast<const TI *>(pa.Q);
+    a.K = static_cast<const TI *>(pa.K);
+    a.V = static_cast<const TI *>(pa.V);
     a.alpha = static_cast<const float *>(pa.alpha);
-    a.Y = static_cast<float *>(pa.Y);
+    a.Y = static_cast<TI *>(pa.Y);
     a.S = static_cast<float *>(pa.S);
     a.z = static_cast<float *>(pa.z);
     a.T = pa.T;
     a.eps = (float)pa.eps;
     int64_t nseg, seg_len;
-    if (!plan_segments(pa.n_heads, pa.T, kFC, kD * 4, &nseg, &seg_len))
+    if (!plan_segments(pa.n_heads, pa.T, kFC, D * (int64_t)sizeof(TI), segment_slot_bytes(D), &nseg, &seg_len))
         return hipErrorInvalidValue;
     a.nseg = (int)nseg;
     a.seg_len = seg_len;
     return dispatch_feature_map(pa.phi, [&](auto fm) {
         constexpr int FM = decltype(fm)::value;
-        return pa.alpha ? launch_f32<true, FM>(a, pa.n_heads, stream) : launch_f32<false, FM>(a, pa.n_heads, stream);
+        return pa.alpha ? launch_f32<TI, D, true, FM>(a, pa.n_heads, stream)
+                        : launch_f32<TI, D, false, FM>(a, pa.n_heads, stream);
     });
+}
+
+bool aligned(const void *p, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0; }
+
+}  // namespace
+
+bool mfma_f32_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk)
+{
+    if (chunk != kFC || d != dv)
+        return false;
+    return (io_dtype == LA_F32 && (d == 64 || d == 128)) || (io_dtype == LA_BF16 && d == 64);
+}
+
+hipError_t launch_prefill_mfma_f32(const PrefillArgs &pa, la_dtype io_dtype, hipStream_t stream)
+{
+    // rows are read and written 4 elements at a time: 16 bytes for fp32, 8 for bf16
+    const uintptr_t al = io_dtype == LA_F32 ? 16 : 8;
+    if (!aligned(pa.Q, al) || !aligned(pa.K, al) || !aligned(pa.V, al) || !aligned(pa.Y, al))
+        return launch_prefill_general(pa, io_dtype, stream);
+    if (io_dtype == LA_BF16)
+        return launch_typed<bf16, 64>(pa, stream);
+    return pa.d == 64 ? launch_typed<float, 64>(pa, stream) : launch_typed<float, 128>(pa, stream);
 }
 
 }  // namespace la

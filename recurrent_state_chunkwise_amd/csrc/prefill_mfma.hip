@@ -48,8 +48,6 @@ namespace {
 constexpr int64_t kSegmentTarget = 256;
 
 // per-(sequence, segment) slot in Y: S [128][128], z [128], segment gate product, pad
-constexpr int kSlotFloats = kD * kD + kD + 4;
-constexpr int64_t kMinSegTokens = (kSlotFloats * 4 + kD * 2 - 1) / (kD * 2);
 
 struct Args {
     const bf16 *Q, *K, *V;
@@ -1431,14 +1429,15 @@ hipError_t launch_nc(const Args &a, int64_t n_heads, hipStream_t stream)
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Segments per sequence: enough (sequence, segment) workgroups to give every compute
-// unit work, each segment a whole number of chunks and long enough to hold its slot in
-// Y (rows of bf16, the shorter kind), every segment (the last may be up to twice as long)
-// below 2^31 bytes of Q rows of row_bytes each so that buffer offsets stay 32-bit.
+// unit work, each segment a whole number of chunks and long enough to hold its slot of
+// slot_bytes in its rows of Y, every segment (the last may be up to twice as long) below
+// 2^31 bytes of Q rows of row_bytes each so that buffer offsets stay 32-bit.
 // Returns 0 when the grid would not fit or a segment could not be kept that short.
-int64_t choose_segments(int64_t T, int64_t n_heads, int C, int64_t target, int64_t row_bytes)
+int64_t choose_segments(int64_t T, int64_t n_heads, int C, int64_t target, int64_t row_bytes, int64_t slot_bytes)
 {
     int64_t nseg = (target + n_heads - 1) / n_heads;
-    const int64_t min_len = ((kMinSegTokens + C - 1) / C) * C;
+    const int64_t min_tokens = (slot_bytes + row_bytes - 1) / row_bytes;
+    const int64_t min_len = ((min_tokens + C - 1) / C) * C;
     if (nseg > T / min_len)
         nseg = T / min_len;
     const int64_t max_len = ((int64_t)1 << 31) / row_bytes / 2;
@@ -1456,16 +1455,17 @@ int64_t choose_segments(int64_t T, int64_t n_heads, int C, int64_t target, int64
 
 }  // namespace
 
-bool plan_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t row_bytes, int64_t *nseg, int64_t *seg_len)
+bool plan_segments(int64_t n_heads, int64_t T, int32_t chunk, int64_t row_bytes, int64_t slot_bytes, int64_t *nseg,
+                   int64_t *seg_len)
 {
-    *nseg = choose_segments(T, n_heads, chunk, kSegmentTarget, row_bytes);
+    *nseg = choose_segments(T, n_heads, chunk, kSegmentTarget, row_bytes, slot_bytes);
     if (*nseg == 0)
         return false;
     *seg_len = *nseg == 1 ? T : ((T / *nseg) / chunk) * chunk;  // the last segment takes the rest
     return true;
 }
 
-int64_t segment_slot_bytes() { return (int64_t)kSlotFloats * 4; }
+int64_t segment_slot_bytes(int32_t d) { return ((int64_t)d * d + d + 4) * 4; }
 
 bool mfma_prefill_supported(la_dtype io_dtype, int32_t d, int32_t dv, int32_t chunk)
 {
@@ -1494,7 +1494,7 @@ hipError_t launch_noncausal_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
     a.eps = (float)pa.eps;
     int64_t nseg, seg_len;
     const int64_t bph = (pa.T + kNcBlockTokens - 1) / kNcBlockTokens;
-    if (!plan_segments(pa.n_heads, pa.T, kPcC, kD * 2, &nseg, &seg_len) || pa.n_heads * bph > INT32_MAX)
+    if (!plan_segments(pa.n_heads, pa.T, kPcC, kD * 2, segment_slot_bytes(kD), &nseg, &seg_len) || pa.n_heads * bph > INT32_MAX)
         return hipErrorInvalidValue;
     a.nseg = (int)nseg;
     a.seg_len = seg_len;
@@ -1518,7 +1518,7 @@ hipError_t launch_prefill_mfma_bf16(const PrefillArgs &pa, hipStream_t stream)
 
     const int C = pa.chunk;
     int64_t nseg, seg_len;
-    if (!plan_segments(pa.n_heads, pa.T, C, kD * 2, &nseg, &seg_len))
+    if (!plan_segments(pa.n_heads, pa.T, C, kD * 2, segment_slot_bytes(kD), &nseg, &seg_len))
         return hipErrorInvalidValue;
     a.nseg = (int)nseg;
     a.seg_len = seg_len;

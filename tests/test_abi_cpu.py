@@ -135,7 +135,12 @@ def test_prefill_variant(lib):
     assert la.la_prefill_variant(F64, 16, 16, 16, False, F64) == 0
     assert la.la_prefill_variant(F32, 128, 128, 64, True, F32) == 2   # the fp32 MFMA kernel
     assert la.la_prefill_variant(F32, 128, 128, 128, True, F32) == 0  # fp32 at chunk 128: general
-    assert la.la_prefill_variant(F32, 64, 64, 64, False, F32) == 0
+    assert la.la_prefill_variant(F32, 64, 64, 64, False, F32) == 2     # d = 64: fp32 MFMA, either io
+    assert la.la_prefill_variant(BF16, 64, 64, 64, True, F32) == 2
+    assert la.la_prefill_variant(BF16, 64, 64, 128, True, F32) == 0
+    assert la.la_prefill_variant(F32, 64, 128, 64, True, F32) == 0
+    assert la.la_prefill_variant(F64, 64, 64, 64, True, F64) == 0
+    assert la.la_prefill_variant(BF16, 96, 96, 64, False, F32) == 0
     assert la.la_prefill_variant(BF16, 128, 128, 64, False, F32) == 1
     assert la.la_prefill_variant(BF16, 128, 128, 128, True, F32) == 1
     assert la.la_prefill_variant(BF16, 128, 128, 32, True, F32) == 0
@@ -301,20 +306,24 @@ PLAN_H = [1, 2, 3, 4, 31, 32, 64, 100, 255, 256, 257, 4096, 65536, 1 << 20, (1 <
 INT32_MAX = (1 << 31) - 1
 
 
-@pytest.mark.parametrize("chunk", [64, 128])
-def test_segment_plan_invariants(lib, chunk):
-    """The plan of the bf16 MFMA prefill at extreme lengths and head counts: whole chunks,
-    every segment's own rows of Y hold its state slot, 32-bit offsets inside a segment, a grid
+# (io dtype, width d = dv, chunk, bytes of one row of Q) of every MFMA prefill plan
+PLANS = [(BF16, 128, 64, 256), (BF16, 128, 128, 256), (F32, 128, 64, 512), (F32, 64, 64, 256),
+         (BF16, 64, 64, 128)]
+
+
+@pytest.mark.parametrize("io,d,chunk,row", PLANS)
+def test_segment_plan_invariants(lib, io, d, chunk, row):
+    """The plan of the MFMA prefills at extreme lengths and head counts: whole chunks, every
+    segment's own rows of Y hold its state slot, 32-bit offsets inside every segment, a grid
     that fits one launch, the compute units filled when the length allows, and no more
     segments than needed."""
-    slot = la.la_prefill_segment_slot_bytes()
-    assert slot == (128 * 128 + 128 + 4) * 4  # S, z and the segment's gate product, padded
-    row = 128 * 2                              # bytes of one token's row of Q, K, V or Y
+    slot = la.la_prefill_segment_slot_bytes(d)
+    assert slot == (d * d + d + 4) * 4       # S, z and the segment's gate product, padded
     min_len = -(-(-(-slot // row)) // chunk) * chunk  # shortest segment that holds a slot
     max_len = (1 << 31) // row // 2            # longest segment but the last: below 2^30 bytes
     for T in PLAN_T:
         for H in PLAN_H:
-            nseg, seg_len = la.la_prefill_segments(H, T, chunk)
+            nseg, seg_len = la.la_prefill_segments(H, T, chunk, io, d)
             if nseg == 0:  # refused: even the fewest segments would not fit one grid
                 assert H * -(-T // max_len) > INT32_MAX, (T, H)
                 continue
@@ -337,7 +346,10 @@ def test_segment_plan_rejections(lib):
     assert la.la_prefill_segments(0, 100, 64)[0] == -1
     assert la.la_prefill_segments(4, 0, 64)[0] == -1
     assert la.la_prefill_segments(4, 100, 32)[0] == -1
-    assert lib.la_prefill_segments(BF16, 4, 100, 64, None) == -1
+    assert lib.la_prefill_segments(BF16, 128, 4, 100, 64, None) == -1
+    assert la.la_prefill_segments(4, 100, 64, BF16, 96)[0] == -1   # no MFMA prefill at d = 96
+    assert la.la_prefill_segments(4, 100, 128, BF16, 64)[0] == -1  # d = 64 runs chunk 64 only
+    assert la.la_prefill_segment_slot_bytes(96) == -1
     # the full workloads: one segment per compute unit (or per sequence past 256 sequences)
     assert la.la_prefill_segments(64, 4096, 64) == (4, 1024)
     assert la.la_prefill_segments(32, 16384, 64) == (8, 2048)
@@ -347,6 +359,11 @@ def test_segment_plan_rejections(lib):
     assert la.la_prefill_segments(64, 4096, 64, F32) == (4, 1024)
     assert la.la_prefill_segments(64, 4096, 128, F32)[0] == -1
     assert la.la_prefill_segments(64, 4096, 64, F64)[0] == -1
+    # d = 64 (16,656-byte slots): the state builds of the history-against-state comparison,
+    # 8 sequences of 8,191 tokens cut into 32 segments of 192, and 1,024 sequences uncut
+    assert la.la_prefill_segments(8, 8191, 64, BF16, 64) == (32, 192)
+    assert la.la_prefill_segments(1024, 8191, 64, BF16, 64) == (1, 8191)
+    assert la.la_prefill_segments(8, 8191, 64, F32, 64) == (32, 192)
 
 
 def test_segment_plan_f32_rows(lib):
@@ -360,4 +377,4 @@ def test_segment_plan_f32_rows(lib):
             last = T - (nseg - 1) * seg_len
             assert last * 512 < (1 << 31) and seg_len * 512 < (1 << 31), (T, H, nseg, seg_len)
             if nseg > 1:
-                assert seg_len % 64 == 0 and seg_len * 512 >= la.la_prefill_segment_slot_bytes()
+                assert seg_len % 64 == 0 and seg_len * 512 >= la.la_prefill_segment_slot_bytes(128)

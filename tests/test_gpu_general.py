@@ -81,7 +81,7 @@ GENERAL_CASES = [
     (1, 2, 37, 16, 16, 8, False, False),
     (2, 3, 100, 32, 24, 16, True, True),
     (1, 1, 1, 5, 3, 4, True, True),
-    (1, 2, 200, 128, 128, 64, False, True),
+    (1, 2, 200, 128, 128, 48, False, True),
     (1, 2, 300, 128, 128, 128, True, False),
     (2, 1, 129, 64, 40, 32, True, True),
     (1, 1, 65, 128, 17, 3, False, False),
@@ -113,8 +113,10 @@ def _case_inputs(torch, B, H, T, d, dv, gated, with_state, dtype, seed):
 def test_general_prefill_parity(torch, case, io):
     B, H, T, d, dv, chunk, gated, with_state = case
     dtype = wl.torch_dtype(io)
-    if io == "bf16" and la.la_prefill_variant(la.LA_BF16, d, dv, chunk, gated, la.LA_F32) != 0:
-        pytest.skip("this bf16 shape runs the MFMA kernel (covered by its own tests)")
+    code = {"f32": la.LA_F32, "f64": la.LA_F64, "bf16": la.LA_BF16}[io]
+    state = la.LA_F64 if io == "f64" else la.LA_F32
+    if la.la_prefill_variant(code, d, dv, chunk, gated, state) != 0:
+        pytest.skip("this shape runs an MFMA kernel (covered by its own tests)")
     Q, K, V, alpha, S0, z0 = _case_inputs(torch, B, H, T, d, dv, gated, with_state, dtype, 1000 + T + d)
     Y, S, z = _run_prefill(torch, Q, K, V, alpha, 1e-6, chunk, S0, z0)
     ref = oracle_prefill(Q, K, V, alpha, 1e-6, S0, z0)

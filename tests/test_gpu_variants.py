@@ -1,8 +1,9 @@
 """GPU parity of the feature-map variants and of the non-causal form against the
 FP64 oracle, through the C ABI.
 
-Feature maps relu+1, relu+1e-5 and sigmoid+1e-5 (and ELU+1) on the causal MFMA prefill
-(chunk 64 and 128, gated and ungated), the general prefill (f32, f64), the decode step
+Feature maps relu+1, relu+1e-5 and sigmoid+1e-5 (and ELU+1) on the causal bf16 MFMA prefill
+(chunk 64 and 128, gated and ungated), the fp32-arithmetic MFMA prefill (f32 at widths 128
+and 64, bf16 at 64), the general prefill (f32, f64), the decode step
 (bf16 at width 128, f32 general) and the non-causal form: the bf16 MFMA path with one
 and several segments, ragged lengths (below one 16-token tile, across read-out blocks),
 a carried incoming state, and the general path in f32, f64 and bf16 at other widths;
@@ -83,6 +84,9 @@ CAUSAL = [
     (2, 2, 77, 16, 24, "f32", 16, True, True),
     (1, 2, 50, 8, 8, "f64", 7, False, True),
     (1, 1, 1500, 128, 128, "bf16", 128, False, True),  # several segments at chunk 128
+    (1, 2, 700, 128, 128, "f32", 64, True, True),      # the fp32-arithmetic MFMA kernel from here
+    (1, 2, 500, 64, 64, "bf16", 64, True, True),
+    (1, 1, 400, 64, 64, "f32", 64, False, True),
 ]
 
 
