@@ -47,12 +47,24 @@ STATE_BYTES = 128 * 128 * 4 + 128 * 4
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+_BF16_PREFILL = ["prefill_mfma.hip", "prefill_common.hpp", "kernels_general.hip"]
 KERNEL_SOURCES = {
-    "prefill": ["prefill_mfma.hip", "kernels_general.hip"],
+    "prefill": _BF16_PREFILL,
+    "gated": _BF16_PREFILL,
+    "long": _BF16_PREFILL,
+    "noncausal": _BF16_PREFILL,
+    "fp32": ["prefill_f32.hip", "prefill_common.hpp", "kernels_general.hip"],
     "decode": ["kernels_general.hip"],
     "delta": ["delta_decode.hip"],
-    "noncausal": ["prefill_mfma.hip", "kernels_general.hip"],
 }
+
+
+_T0 = time.perf_counter()
+
+
+def progress(msg):
+    """One line on stderr per finished leg, so that a long run shows where it is."""
+    print("[bench %6.1f s] %s" % (time.perf_counter() - _T0, msg), file=sys.stderr, flush=True)
 
 
 def source_digest(kind):
@@ -555,6 +567,7 @@ def main():
     torch.cuda.synchronize()
     main_t = time_prefill(torch, la, wl, cfg, args.steps, args.warmup)
     total_ms, call_ms = main_t["total_ms"], main_t["call_ms"]
+    progress("ungated prefill timed")
     # the same call on one input set, whose inputs may stay in the last-level cache (reported only)
     warm_call_ms = None
     if args.only is None:
@@ -608,6 +621,7 @@ def main():
     if not args.no_extra:
         dcfg = wl.DECODE
         d_total, d_call = time_decode(torch, la, wl, dcfg)
+        progress("decode timed")
         d_bytes = dcfg.n_states * (2 * STATE_BYTES + 3 * 256 + 256)
         out["decode"] = {
             "workload": dcfg.name, "steps": dcfg.steps,
@@ -621,6 +635,7 @@ def main():
         }
         xcfg = wl.DELTA_DECODE
         x_total, x_call = time_delta(torch, la, wl, xcfg)
+        progress("delta-rule decode timed")
         x_bytes = xcfg.n_states * DELTA_STATE_STEP_BYTES
         out["delta_decode"] = {
             "workload": xcfg.name, "steps": xcfg.steps,
@@ -633,6 +648,7 @@ def main():
                          "call_ms": x_call, "algorithmic_bytes": x_bytes},
         }
         n_call = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, noncausal=True)["call_ms"]
+        progress("non-causal form timed")
         out["noncausal"] = {
             "workload": "noncausal_" + cfg.name, "value": tokens / (n_call / 1e3), "unit": "tokens/s",
             "roofline": {"kernel": "la_prefill_noncausal (segment sums + read-out)", "bound": "hbm",
@@ -643,14 +659,17 @@ def main():
         }
         out["kv_vs_state"] = time_kv_state(torch, la, wl, wl.KV_STATE)
         out["kv_vs_state_batched"] = time_kv_state(torch, la, wl, wl.KV_STATE_BATCHED)
+        progress("history-against-state comparison timed")
         other = []
-        for ocfg in (wl.PREFILL_GATED, wl.PREFILL_LONG):
+        for kind, ocfg in (("gated", wl.PREFILL_GATED), ("long", wl.PREFILL_LONG)):
             o_call = time_prefill(torch, la, wl, ocfg, args.steps, args.warmup)["call_ms"]
             ob = prefill_bytes(ocfg.B, ocfg.H, ocfg.T, ocfg.gated)
             of = prefill_useful_flops(ocfg.B, ocfg.H, ocfg.T, ocfg.chunk)
             other.append({"workload": ocfg.name, "value": ocfg.B * ocfg.T / (o_call / 1e3), "unit": "tokens/s",
                           "call_ms": o_call, "hbm_frac": ob / (o_call / 1e3) / 1e9 / HBM_PEAK_GBS,
-                          "mfma_frac": of / (o_call / 1e3) / 1e12 / BF16_PEAK_TFLOPS})
+                          "mfma_frac": of / (o_call / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+                          "algorithmic_bytes": ob, "traffic": measured_traffic(kind)})
+            progress("%s timed" % ocfg.name)
         # the fp32-input path on the ungated shape: its useful flops at the fp32 matrix peak
         # take longer than its bytes at the HBM peak, so that is its roofline
         fcfg = wl.PREFILL_UNGATED_F32
@@ -662,8 +681,10 @@ def main():
                       "roofline": {"bound": "mfma", "achieved": ff / (f_call / 1e3) / 1e12, "peak": FP32_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": ff / (f_call / 1e3) / 1e12 / FP32_PEAK_TFLOPS,
                                    "hbm_frac": fb / (f_call / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                   "algorithmic_bytes": fb, "useful_flops": ff}})
+                                   "algorithmic_bytes": fb, "useful_flops": ff,
+                                   "traffic": measured_traffic("fp32")}})
         out["other"] = other
+        progress("fp32-input prefill timed")
     if not args.no_extra:
         ceil = measured_ceilings(torch)
         out["measured_ceilings"] = ceil
@@ -676,6 +697,7 @@ def main():
         out["decode"]["roofline"]["measured_ceiling_GBps"] = ceil["copy_GBps"]
         out["decode"]["roofline"]["frac_of_measured"] = out["decode"]["roofline"]["achieved"] / ceil["copy_GBps"]
     if not args.no_cpu_baseline:
+        progress("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(wl, torch)
     print(json.dumps(out), flush=True)
 
