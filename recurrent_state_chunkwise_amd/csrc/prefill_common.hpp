@@ -110,6 +110,23 @@ __device__ __forceinline__ float write_weight(const float *lg, const int *zp, in
     return j >= n ? 0.f : w;
 }
 
+// The same write weight for token `lane` of a chunk of n tokens, formed by the wave that
+// has just scanned the chunk's gates (s: this lane's prefix sum of log alpha, zf: its last
+// zero-gate position), so that the staging reads one stored value instead of two scans and
+// an exponential: the operands and the arithmetic are those of write_weight, bitwise.
+// s_last, z_last: the scans at the chunk's last token n - 1; s: the scan at token j.
+__device__ __forceinline__ float scanned_write_weight(float s_last, int z_last, float s, int n, int j)
+{
+    const float e = __expf(s_last - s);
+    const float w = z_last > j ? 0.f : e;
+    return j >= n ? 0.f : w;
+}
+__device__ __forceinline__ float lane_write_weight(float s, int zf, int n, int lane)
+{
+    const float s_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), n - 1));
+    return scanned_write_weight(s_last, __builtin_amdgcn_readlane(zf, n - 1), s, n, lane);
+}
+
 // Inclusive scans over the 64 lanes of a wave with data-parallel moves (DPP): shifts by 1,
 // 2, 4 and 8 lanes inside each row of 16, then the row totals carried from lane 15 to rows
 // 1 and 3 and from lane 31 to rows 2 and 3.  A lane whose source falls outside its row, or

@@ -168,6 +168,7 @@ struct alignas(16) PcSmem {
     alignas(16) float lg[2][kPcC];
     alignas(16) float gj[2][kPcC];
     alignas(16) int zp[2][kPcC];
+    alignas(16) float wt[GATED ? 2 : 1][GATED ? kPcC : 4];  // write weights of the staged chunk (gated)
 };
 
 template <bool GATED, int FM>
@@ -242,7 +243,8 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
             if (GATED)
                 ar = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b32(rA, (c * C + lane) * 4, 0, kNT));
         };
-        // inclusive scans of log(alpha) and of the last zero-gate position (one wave)
+        // inclusive scans of log(alpha) and of the last zero-gate position, and the write
+        // weights they give (one wave)
         auto scan = [&](int n, int gs, float ar) {
             if (GATED && scanner) {
                 const float av = lane < n ? ar : 1.f;
@@ -253,6 +255,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 sm.lg[gs][lane] = s;
                 sm.zp[gs][lane] = zf;
                 sm.gj[gs][lane] = zf >= 0 ? 0.f : __expf(s);
+                sm.wt[gs][lane] = lane_write_weight(s, zf, n, lane);
             }
         };
         // phi(q) rows and V rows
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
                 float x[8];
                 unpack8(rk[p], x);
                 bf16x8 kb, kwb;
-                const float w = write_weight<GATED>(sm.lg[gs], sm.zp[gs], n, j);
+                const float w = GATED ? sm.wt[gs][j] : write_weight<false>(nullptr, nullptr, n, j);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     const float f = phi<FM>(x[s]);
@@ -587,9 +590,13 @@ struct alignas(16) P8Smem {
     alignas(16) bf16 zhl[2][2][kD];    // z entering the chunk in bf16 high and low parts, by parity
     alignas(16) float zred[3][kD];     // fp32 z update of the chunk from producer waves 9-11
     alignas(16) float dq[kP8C];        // phi(q_j) . z_prev
-    alignas(16) float lg[2][kP8C];
+    // Gate scans of chunk c: lg, zp and the write weights wt are read only in part A of
+    // chunk c (producers' write weights, consumers' score weights) and rewritten for chunk
+    // c + 1 in part B, so one buffer each; the consumers read gj in part B too, so two.
+    alignas(16) float lg[kP8C];
+    alignas(16) int zp[kP8C];
+    alignas(16) float wt[kP8C];
     alignas(16) float gj[2][kP8C];
-    alignas(16) int zp[2][kP8C];
 };
 static_assert(sizeof(P8Smem) <= 160 * 1024, "the chunk-128 tiles must fit in the 160 KB of LDS");
 
@@ -658,20 +665,33 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
             if (GATED && scanner) {
                 float carry = 0.f;
                 int zcarry = -1;
+                float sv2[2];
+                int zf2[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int j = h * 64 + lane;
+                    const int jo = opaque(j);  // addresses formed here, not held across the loop
                     const float av = j < n ? ar[h] : 1.f;
                     float sv = av > 0.f ? __logf(av) : 0.f;
                     int zf = av == 0.f ? j : -1;
                     sv = wave_scan_add(sv) + carry;
                     zf = max(wave_scan_max(zf), zcarry);
-                    sm.lg[gs][j] = sv;
-                    sm.zp[gs][j] = zf;
+                    sm.lg[jo] = sv;
+                    sm.zp[jo] = zf;
                     sm.gj[gs][j] = zf >= 0 ? 0.f : __expf(sv);
                     carry = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv), 63));
                     zcarry = __builtin_amdgcn_readlane(zf, 63);
+                    sv2[h] = sv;
+                    zf2[h] = zf;
                 }
+                // the write weights, from the scans at the chunk's last token n - 1
+                const int l = n - 1;
+                const float s_last = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l >= 64 ? sv2[1] : sv2[0]), l & 63));
+                const int z_last = __builtin_amdgcn_readlane(l >= 64 ? zf2[1] : zf2[0], l & 63);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    sm.wt[opaque(h * 64 + lane)] = scanned_write_weight(s_last, z_last, sv2[h], n, h * 64 + lane);
             }
         };
         // phi(q) and phi(k) rows
@@ -696,7 +716,8 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
         };
         // V rows and the write weights w_j phi(k_j) (w_j = gates after j to the chunk end,
         // 0 past the end of the segment)
-        auto stage_vw = [&](int gs, int n) {
+        auto stage_vw = [&](int n) {
+            const float *wts = sm.wt + opaque(0);  // addressed afresh each chunk
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 zsum[e] = 0.f;
@@ -704,7 +725,7 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
             for (int p = 0; p < TPT; ++p) {
                 const int j = tg * TPT + p;
                 *reinterpret_cast<uint4 *>(&sm.Vs[pr_off(j, fg * 8)]) = rv[p];
-                const float w = write_weight<GATED>(sm.lg[gs], sm.zp[gs], n, j);
+                const float w = GATED ? wts[j] : write_weight<false>(nullptr, nullptr, n, j);
                 float x[8];
                 unpack8(rk[p], x);
                 bf16x8 kwb;
@@ -760,7 +781,7 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
         // are issued unconditionally so that every wait on them is a counted one.
         for (int c = 0; c < n_chunks; ++c) {
             // part A of chunk c
-            stage_vw(c & 1, chunk_len(c));
+            stage_vw(chunk_len(c));
             load(rV, c + 1, rv);
             load(rK, c + 1, rk);
             wg_barrier();  // a | b
@@ -860,7 +881,7 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
             for (int r = 0; r < 4; ++r)
                 ii[r] = ti * 16 + sigma(lg4 * 4 + r);
             float dec[4];
-            pair_decays<GATED>(sm.lg[buf], sm.zp[buf], j, ii, dec);
+            pair_decays<GATED>(sm.lg + opaque(0), sm.zp + opaque(0), j, ii, dec);
             f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kf = 0; kf < 4; ++kf) {
@@ -989,6 +1010,7 @@ struct alignas(16) SumSmem {
     alignas(16) float lg[3][kPcC];
     alignas(16) float gj[3][kPcC];
     alignas(16) int zp[3][kPcC];
+    alignas(16) float wt[GATED ? 3 : 1][GATED ? kPcC : 4];  // write weights (gated)
 };
 
 // NONCAUSAL (ungated): every segment's map is needed, including the last one's, and it
@@ -1058,6 +1080,7 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
                 sm.lg[gs][lane] = s;
                 sm.zp[gs][lane] = zf;
                 sm.gj[gs][lane] = zf >= 0 ? 0.f : __expf(s);
+                sm.wt[gs][lane] = lane_write_weight(s, zf, n, lane);
             }
         };
         // write weights w phi(k) in bf16 (Ws, the operand of S), 0 past the end of the
@@ -1067,7 +1090,7 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
 #pragma unroll
             for (int p = 0; p < TPT; ++p) {
                 const int j = tg * TPT + p;
-                const float w = write_weight<GATED>(sm.lg[gs], sm.zp[gs], n, j);
+                const float w = GATED ? sm.wt[gs][j] : write_weight<false>(nullptr, nullptr, n, j);
                 float x[8];
                 unpack8(rkx[p], x);
                 bf16x8 kb;
