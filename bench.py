@@ -129,10 +129,11 @@ def run_for(torch, fn, at_least_calls, floor_s):
         batch = max(1, int((floor_s - el) / (el / n) * 1.1) + 1)
 
 
-def time_prefill(torch, la, wl, cfg, steps, warmup, sets=2, noncausal=False):
+def time_prefill(torch, la, wl, cfg, steps, warmup, sets=2, noncausal=False, phi=None):
     """Time la_prefill_chunked (or la_prefill_noncausal); step i uses input set i % sets.
     Two sets of the ungated workload (2 x 201 MB of Q, K, V) exceed the 256 MB last-level
     cache, so a timed call cannot find its inputs left there by the previous call.
+    phi: a feature-map name for la_prefill_chunked_fm (None: la_prefill_chunked, ELU+1).
 
     Returns a dict:
       total_ms  exactly `steps` steps of state initialisation + call, events only around
@@ -151,6 +152,8 @@ def time_prefill(torch, la, wl, cfg, steps, warmup, sets=2, noncausal=False):
         Q, K, V, A = inputs[i % sets]
         if noncausal:
             la.la_prefill_noncausal(Q, K, V, cfg.eps, Y, S, z)
+        elif phi is not None:
+            la.la_prefill_chunked_fm(Q, K, V, A, cfg.eps, cfg.chunk, Y, S, z, phi=phi)
         else:
             la.la_prefill_chunked(Q, K, V, A, cfg.eps, cfg.chunk, Y, S, z)
 
@@ -657,6 +660,11 @@ def main():
                          "traffic": measured_traffic("noncausal"),
                          "call_ms": n_call, "algorithmic_bytes": nbytes},
         }
+        # the other feature maps on the same call (template instantiations of the same kernels)
+        out["feature_maps"] = {"workload": cfg.name, "unit": "ms per call", "elu1": call_ms}
+        for fm in ("relu1", "relu_eps", "sigmoid_eps"):
+            out["feature_maps"][fm] = time_prefill(torch, la, wl, cfg, args.steps, args.warmup, phi=fm)["call_ms"]
+        progress("feature maps timed")
         out["kv_vs_state"] = time_kv_state(torch, la, wl, wl.KV_STATE)
         out["kv_vs_state_batched"] = time_kv_state(torch, la, wl, wl.KV_STATE_BATCHED)
         progress("history-against-state comparison timed")
