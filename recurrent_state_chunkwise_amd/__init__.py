@@ -372,7 +372,8 @@ def la_softmax_decode_step_static(q, k, v, pos: int, K_cache, V_cache, y, scale=
 
 
 def la_prefill_variant(io_dtype: int, d: int, dv: int, chunk: int, gated: bool, state_dtype: int) -> int:
-    """1 = bf16 MFMA kernel, 2 = fp32 MFMA kernel, 0 = general kernel, -1 = rejected."""
+    """1 = bf16 MFMA kernel, 2 = fp32-arithmetic MFMA kernel (chunk 64: fp32 io at d = 64 or 128,
+    bf16 io at d = 64), 0 = general kernel, -1 = rejected."""
     return int(library().la_prefill_variant(io_dtype, d, dv, chunk, int(bool(gated)), state_dtype))
 
 

@@ -25,17 +25,18 @@
 // caller's output buffer Y inside the segment they belong to (each needs 66 KB, less
 // than one segment's share of Y); pass 3 reads its slot before it writes any output.
 //
-// Inside a workgroup (8 waves, all 128 value columns) every product is
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
+// Inside a workgroup (8 consumer waves for all 128 value columns, and producer waves that
+// stage the tiles) every product is v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
 //   (1) scores K~ Q~^T, 16x16 tiles on or below the diagonal spread over the waves; the
 //       fp32 tile is masked, gate-weighted and kept in LDS as bf16 in accumulator layout;
-//   (2) N^T  = S_prev^T Q~^T  and  D = z_prev^T Q~^T, both scaled by exp(L_j);
+//   (2) N^T  = S_prev^T Q~^T  and  D = z_prev^T Q~^T (z_prev as bf16 high and low parts),
+//       both scaled by exp(L_j);
 //   (3) N^T += V^T P^T        and  D += 1^T P^T (the row sums of the masked scores);
-//   (4) S = g_last S + (w K~)^T V  and  z = g_last z + (w K~)^T 1.
-// Wave w owns value columns 16w..16w+15 of N and of S and features 16w..16w+15 of z,
-// so S and z never leave registers; z goes through LDS once per chunk for (2).  The
-// outputs are computed transposed so that a lane holds four adjacent columns of one
-// token together with that token's denominator.
+//   (4) S = g_last S + (w K~)^T V.
+// Wave w owns value columns 16w..16w+15 of N and of S, so S never leaves registers.  z is
+// kept by the producers: the fp32 sum of the write weights w phi(k) they form, before the
+// rounding to bf16 that S's operand takes.  The outputs are computed transposed so that a
+// lane holds four adjacent columns of one token together with that token's denominator.
 #include "device_common.hpp"
 #include "internal.hpp"
 #include "prefill_common.hpp"
@@ -43,11 +44,10 @@
 namespace la {
 namespace {
 
-// (sequence, segment) workgroups aimed for: one per compute unit (more segments, two
-// rounds of workgroups, measured slower)
+// (sequence, segment) workgroups aimed for: one per compute unit (twice as many, two
+// rounds of workgroups, and half as many, twice the chunks per workgroup, both measured
+// slower)
 constexpr int64_t kSegmentTarget = 256;
-
-// per-(sequence, segment) slot in Y: S [128][128], z [128], segment gate product, pad
 
 struct Args {
     const bf16 *Q, *K, *V;
@@ -60,6 +60,8 @@ struct Args {
     float eps;
 };
 
+// slot p of a sequence: S [128][128], z [128] and the segment's gate product (padded), in
+// the first rows of segment p of Y
 __device__ __forceinline__ float *slot_ptr(const Args &a, int64_t head, int p)
 {
     return reinterpret_cast<float *>(a.Y + (head * a.T + (int64_t)p * a.seg_len) * kD);
@@ -67,13 +69,14 @@ __device__ __forceinline__ float *slot_ptr(const Args &a, int64_t head, int p)
 
 // ============================================================================ pass 3, chunk 64
 // Producer / consumer form of the full pass at chunk 64: 12 waves, of which waves 0-7
-// (consumers) hold S and z and do every product, while waves 8-11 (producers) turn the
-// raw Q, K, V and alpha of the next chunk into staged tiles in the other half of a
-// double-buffered LDS.  Two workgroup barriers per chunk i:
+// (consumers) hold S and do every product, while waves 8-11 (producers) turn the raw Q,
+// K, V and alpha of the next chunk into staged tiles in the other half of a
+// double-buffered LDS and keep z.  Two workgroup barriers per chunk i:
 //   part a   consumers: scores of chunk i; N^T = S_prev^T Q~^T; waves 4-7 D = z_prev^T Q~^T
-//            producers: y of chunk i-1 to HBM; gate scan of chunk i+1; phi(q) and V of chunk i+1
-//   part b   consumers: gates, V^T P^T and 1^T P^T, y into LDS, state and z update
-//            producers: phi(k) and the write weights of chunk i+1
+//            producers: z entering chunk i+1; y of chunk i-1 to HBM; gate scan (and write
+//            weights) of chunk i+1; phi(q) and V of chunk i+1
+//   part b   consumers: gates, V^T P^T and 1^T P^T, y into LDS, state update
+//            producers: phi(k), the write weights and their fp32 sums for z, of chunk i+1
 // Each raw load is issued two chunks ahead of its use, except K in the gated form, which
 // has one register set and is loaded one chunk ahead: the gated producers also hold the
 // fp32 sums of the z update, and a second K set would not fit in their registers.  The two
