@@ -8,6 +8,15 @@ cycle, 16-byte reads 16 lanes per cycle, and writes at 128 bytes per cycle (8 la
 16 bytes, 16 lanes of 8 bytes).  Within the lanes served in one cycle, two different
 four-byte words in one bank conflict; lanes reading the same word do not.
 
+Where the model stops: a later probe (SQ_LDS_BANK_CONFLICT per instruction) confirmed it
+for the 8-byte and transposing reads and the 16-byte row stores of the staged tiles (no
+conflicts at 272-byte rows) and for contiguous or 16-granule-swizzled 16-byte reads, but
+the 16-byte score operand reads, 16 rows of 272 bytes with lane group g taking granule g,
+cost about 4 extra cycles per read on the device (none at 288-byte rows, where the 8-byte
+reads conflict instead).  Those reads are therefore not claimed conflict-free here
+(`score_reads` below is left out of the check); reading them as two 8-byte halves removes
+the conflicts but measured slower in every output pass, so the kernels keep them.
+
 The index formulas below restate the kernels' own: a staged tile holds one token row of
 128 bf16 per token, padded to 136 elements (272 bytes); lane = (lg4, lr) with lane =
 16 lg4 + lr; the transposing load takes, in each 16-lane group, 4 adjacent columns
@@ -153,14 +162,14 @@ def kernel_patterns():
     # chunk-64 output pass: 4 producer waves, 4 tokens per thread and tile
     for name, addrs, (w, lpc) in producer_stores(4, 4):
         yield "pc " + name, addrs, w, lpc
-    for gen in (inter_chunk_reads(4), score_reads(4), intra_value_reads(2), state_update_reads(2),
+    for gen in (inter_chunk_reads(4), intra_value_reads(2), state_update_reads(2),
                 score_tile_accesses(6), y_tile_accesses(4)):
         for name, addrs, (w, lpc) in gen:
             yield "pc " + name, addrs, w, lpc
     # chunk-128 output pass: 4 producer waves, 8 tokens per thread and tile
     for name, addrs, (w, lpc) in producer_stores(8, 4):
         yield "p8 " + name, addrs, w, lpc
-    for gen in (inter_chunk_reads(8), score_reads(8), intra_value_reads(4), state_update_reads(4)):
+    for gen in (inter_chunk_reads(8), intra_value_reads(4), state_update_reads(4)):
         for name, addrs, (w, lpc) in gen:
             yield "p8 " + name, addrs, w, lpc
     # segment-map pass (chunk 64): stores of the write weights and V, then (4)
@@ -178,7 +187,7 @@ def test_every_kernel_access_is_conflict_free():
         checked += 1
         if e:
             bad.append((name, e))
-    assert checked > 300
+    assert checked > 200
     assert not bad, bad[:10]
 
 
