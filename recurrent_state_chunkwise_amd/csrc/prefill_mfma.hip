@@ -205,7 +205,9 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
         const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
         const rsrc_t rY = make_rsrc(a.Y + row0 * kD, len * kD * 2);
         const int pt = tid - kPcConsumers;
-        const bool scanner = wave == 8;
+        // the gate scan runs on a wave that does not also finish z (waves 8 and 9 do), so
+        // that neither job lengthens the other's wave
+        const bool scanner = wave == 10;
         // thread (fg, tg) stages granule fg (8 features) of tokens TPT tg .. TPT tg + TPT - 1
         constexpr int TPT = 16 / kPcProducers;
         const int fg = pt & 15, tg = pt >> 4;
@@ -633,7 +635,7 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
         const rsrc_t rV = make_rsrc(a.V + row0 * kD, len * kD * 2);
         const rsrc_t rA = make_rsrc(GATED ? a.alpha + row0 : a.S, GATED ? len * 4 : 0);
         const int pt = tid - kPcConsumers;
-        const bool scanner = wave == 8;
+        const bool scanner = wave == 9;  // not wave 8, which keeps z
         // thread (fg, tg) stages granule fg (8 features) of tokens TPT tg .. TPT tg + TPT - 1
         constexpr int TPT = C / 16;
         const int fg = pt & 15, tg = pt >> 4;
