@@ -874,32 +874,54 @@ __global__ __launch_bounds__(kP8Threads) void prefill_p8_kernel(Args a)
                 d = mfma(zl, qv, d);
             }
         }
-        for (int k = wave; k < G::NPT; k += 8) {
-            int tj = 0;
-            while ((tj + 1) * (tj + 2) / 2 <= k)
-                ++tj;
-            const int ti = k - tj * (tj + 1) / 2;
-            // acc[r] = score (j = 16tj + lr, i = 16ti + sigma(4lg4 + r))
-            const int j = tj * 16 + lr;
-            int ii[4];
+        // the score tiles k = wave + 8m of the 36 on or below the diagonal: two at a time with
+        // interleaved product chains (k and k + 8 for k = wave, wave + 16), then the fifth of
+        // waves 0-3 (k = wave + 32) alone
+        auto score_tiles = [&](auto npair, int k0) {
+            constexpr int NP = decltype(npair)::value;
+            int tj[NP], ti[NP];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                ii[r] = ti * 16 + sigma(lg4 * 4 + r);
-            float dec[4];
-            pair_decays<GATED>(sm.lg + opaque(0), sm.zp + opaque(0), j, ii, dec);
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kf = 0; kf < 4; ++kf) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&sm.Ks[pr_off(ti * 16 + sigma(lr), kf * 32 + lg4 * 8)]);
-                const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&sm.Qs[pr_off(tj * 16 + lr, kf * 32 + lg4 * 8)]);
-                sc = mfma(ka, qb, sc);
+            for (int u = 0; u < NP; ++u) {
+                const int k = k0 + 8 * u;
+                tj[u] = 0;
+                while ((tj[u] + 1) * (tj[u] + 2) / 2 <= k)
+                    ++tj[u];
+                ti[u] = k - tj[u] * (tj[u] + 1) / 2;
             }
-            bf16x4 pk;
+            f32x4 sc[NP];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                pk[r] = static_cast<bf16>(ii[r] <= j ? sc[r] * dec[r] : 0.f);
-            sm.P[k * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
-        }
+            for (int u = 0; u < NP; ++u)
+                sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kf = 0; kf < 4; ++kf)
+#pragma unroll
+                for (int u = 0; u < NP; ++u) {
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&sm.Ks[pr_off(ti[u] * 16 + sigma(lr), kf * 32 + lg4 * 8)]);
+                    const bf16x8 qb = *reinterpret_cast<const bf16x8 *>(&sm.Qs[pr_off(tj[u] * 16 + lr, kf * 32 + lg4 * 8)]);
+                    sc[u] = mfma(ka, qb, sc[u]);
+                }
+#pragma unroll
+            for (int u = 0; u < NP; ++u) {
+                // sc[u][r] = score (j = 16tj + lr, i = 16ti + sigma(4lg4 + r))
+                const int j = tj[u] * 16 + lr;
+                int ii[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ii[r] = ti[u] * 16 + sigma(lg4 * 4 + r);
+                float dec[4];
+                pair_decays<GATED>(sm.lg + opaque(0), sm.zp + opaque(0), j, ii, dec);
+                bf16x4 pk;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    pk[r] = static_cast<bf16>(ii[r] <= j ? sc[u][r] * dec[r] : 0.f);
+                sm.P[(k0 + 8 * u) * 64 + lane] = *reinterpret_cast<uint2 *>(&pk);
+            }
+        };
+        static_assert(G::NPT == 36, "four pairs and four lone tiles over the eight waves");
+        score_tiles(std::integral_constant<int, 2>{}, wave);
+        score_tiles(std::integral_constant<int, 2>{}, wave + 16);
+        if (wave < 4)
+            score_tiles(std::integral_constant<int, 1>{}, wave + 32);
         if (lg4 == 0)
             sm.dq[wave * 16 + lr] = d[0];
         wg_barrier();  // a | b
