@@ -415,12 +415,7 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
     wg_barrier();
     wg_barrier();
 
-    for (int i = 0; i < n_steps; ++i) {
-        if (i >= n_chunks) {  // the trailing empty step of an odd chunk count
-            wg_barrier();
-            wg_barrier();
-            break;
-        }
+    for (int i = 0; i < n_chunks; ++i) {
         const int buf = i & 1;
         const int n = chunk_len(i);
         const bf16 *Qb = sm.Qs[buf];
@@ -555,6 +550,10 @@ __global__ __launch_bounds__(kPcThreads) void prefill_pc_kernel(Args a)
             }
         }
         wg_barrier();  // chunk i done
+    }
+    if (n_steps > n_chunks) {  // the trailing empty step of an odd chunk count
+        wg_barrier();
+        wg_barrier();
     }
 
     if (seg != a.nseg - 1)
@@ -1183,11 +1182,7 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
     const int te = lr >> 2, tc = 4 * (lr & 3);
     wg_barrier();
     wg_barrier();
-    for (int i = 0; i < n_steps; ++i) {
-        if (i >= n_chunks) {  // trailing empty steps up to a multiple of the register sets
-            wg_barrier();
-            continue;
-        }
+    for (int i = 0; i < n_chunks; ++i) {
         const int buf = i & 1;
         const bf16 *Wb = sm.Ws[buf];
         const bf16 *Vb = sm.Vs[buf];
@@ -1220,6 +1215,8 @@ __global__ __launch_bounds__(kSumThreads) void summary_pc_kernel(Args a)
         }
         wg_barrier();  // chunk i folded
     }
+    for (int i = n_chunks; i < n_steps; ++i)  // trailing empty steps up to a multiple of the register sets
+        wg_barrier();
 
     // causal: the map goes to the next segment's slot: S, z, then the product of the gates
     float *Sout = slot_ptr(a, head, NONCAUSAL ? seg : seg + 1);
