@@ -521,7 +521,7 @@ def main():
                     help="steps to time with --only decode or --only delta (default: the workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the data-parallel step shards by sequence with no communication); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
